@@ -1,0 +1,404 @@
+#!/usr/bin/env python3
+"""Throughput of rank-major MoE expert-parallel dispatch + combine on one GPU.
+
+    python bench.py [--steps K] [--warmup W] [--workload dsv3]
+
+A step is one round of the hot path over one batch of synthetic input: one
+dispatch (routing, placement, invalid-row fill: one kernel) and one combine
+(gather-reduce: one kernel) through the C ABI of libmoe_ep.so.  Inputs are
+resident in HBM before the timed region.  The expert computation between
+the two (a torch stand-in writing the combine input buffers) runs once per
+instance before timing, so the timed steps are exactly the two launches.
+
+To keep the 256 MB MALL (Infinity Cache) from serving repeated steps, the
+bench rotates over --instances independent copies (workspace, inputs,
+outputs); each DeepSeek-V3-shaped instance touches ~265 MB.
+
+Printed: one JSON line with the whole-job throughput (algorithmic bytes per
+round / wall time per round, the driver's metric), the dominant kernel's
+roofline figures from HIP events recorded around every launch on the launch
+stream, and the CPU oracle's throughput on a bounded sample of the same
+workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine µs/round and effective HBM GB/s (% peak), DSv3 shape"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+KERNEL_SOURCE = os.path.join(ROOT, "combine_token_dest_amd", "csrc", "moe_ep_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{workload}.txt")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes
+# ---------------------------------------------------------------------------
+def algorithmic_bytes(w, n, masks, tpr, has_w):
+    """Bytes the method must move in one round (see the design doc's table):
+    dispatch reads every real token's ids, weights, hidden and scale row once,
+    writes every routed (token, rank) pair's hidden and scale row, and writes
+    the ids (and weights) slot of every receive row of every rank; combine
+    reads every routed pair's expert row and writes every real token's output
+    row."""
+    K, H, S = w.top_k, w.hidden_row_bytes, w.scale_row_bytes
+    O = w.hidden_size * w.combine_elem_bytes
+    N = sum(n)
+    P = int(sum(bin(m).count("1") for m in masks))
+    R = w.ep_size * w.ep_size * tpr
+    wb = 1 if has_w else 0
+    b_dispatch = N * (4 * K * (1 + wb) + H + S) + P * (H + S) + R * 4 * K * (1 + wb)
+    b_combine = P * O + N * O
+    return b_dispatch, b_combine, N, P, R
+
+
+def destination_masks(w, inp):
+    """Per-token destination masks from the inputs (contiguous ownership, the
+    active-rank mask applied); only used to count bytes."""
+    epr = w.num_experts // w.ep_size
+    active = inp.active_rank_mask if inp.active_rank_mask is not None else (1 << w.ep_size) - 1
+    masks = []
+    for s in range(w.ep_size):
+        ids = inp.topk_ids[s]
+        owners = ids // epr
+        for t in range(ids.shape[0]):
+            m = 0
+            for e, o in zip(ids[t], owners[t]):
+                if 0 <= e < w.num_experts:
+                    m |= 1 << int(o)
+            masks.append(m & active)
+    return masks
+
+
+# ---------------------------------------------------------------------------
+# one instance: workspace + inputs + outputs at their own addresses
+# ---------------------------------------------------------------------------
+class Instance:
+    def __init__(self, w, inp, dev_inputs, device):
+        import torch
+        from combine_token_dest_amd import MoEEp, _lib
+        self.w = w
+        self.moe = MoEEp(w.ep_size, w.num_experts, w.top_k, w.max_tokens_per_rank, w.hidden_size,
+                         hidden_row_bytes=w.hidden_row_bytes, scale_row_bytes=w.scale_row_bytes,
+                         combine_max_elem_bytes=w.combine_elem_bytes,
+                         enable_rank_mask=inp.active_rank_mask is not None, device=device)
+        hid, ids, wts, scl = [[t.clone() for t in lst] if lst is not None else None for lst in dev_inputs[:4]]
+        self.inputs = (hid, ids, wts, scl)
+        self.cdtype = torch.float32 if w.combine_dtype == "f32" else torch.bfloat16
+        self.outputs = [torch.empty((n, w.hidden_size), dtype=self.cdtype, device=device)
+                        for n in inp.local_num_tokens]
+        rtpr = inp.runtime_max_tokens_per_rank
+        mask = inp.active_rank_mask
+        # First round through the Python API, with the expert stand-in in between.
+        res = self.moe.dispatch(hid, ids, wts, hidden_states_scale=scl, runtime_max_tokens_per_rank=rtpr,
+                                active_rank_mask=mask)
+        self.tpr = res[0].tokens_per_rank
+        values = dev_inputs[4]
+        for d in range(w.ep_size):
+            buf = self.moe.get_combine_input_buffer(d, self.cdtype)
+            expert_standin_torch(w, d, res[d], values, self.tpr, buf)
+        self.moe.combine([self.moe.get_combine_input_buffer(d, self.cdtype) for d in range(w.ep_size)],
+                         output=self.outputs, active_rank_mask=mask)
+        # Prebuilt C-ABI arguments for the timed steps (same values as above).
+        a = _lib.moe_ep_dispatch_args()
+        for s in range(w.ep_size):
+            n = inp.local_num_tokens[s]
+            a.local_num_tokens[s] = n
+            a.hidden[s] = hid[s].data_ptr() if n else None
+            a.topk_ids[s] = ids[s].data_ptr() if n else None
+            a.topk_weights[s] = wts[s].data_ptr() if n else None
+            if scl is not None:
+                a.hidden_scale[s] = scl[s].data_ptr() if n else None
+        a.weights_present = (1 << w.ep_size) - 1
+        a.scales_present = (1 << w.ep_size) - 1 if scl is not None else 0
+        a.runtime_max_tokens_per_rank = -1 if rtpr is None else rtpr
+        a.active_rank_mask = _lib.MOE_EP_ALL_RANKS if mask is None else mask
+        self.dargs = a
+        c = _lib.moe_ep_combine_args()
+        for s in range(w.ep_size):
+            c.expert_output[s] = None                 # the rank's combine input buffer
+            c.output[s] = self.outputs[s].data_ptr() if inp.local_num_tokens[s] else None
+        c.dtype = _lib.MOE_EP_F32 if w.combine_dtype == "f32" else _lib.MOE_EP_BF16
+        c.active_rank_mask = a.active_rank_mask
+        self.cargs = c
+        self.results = (_lib.moe_ep_dispatch_result * w.ep_size)()
+        self.handle = ctypes.c_void_p(self.moe._handle)
+        self.lib = _lib.load()
+
+    def dispatch(self, stream):
+        st = self.lib.moe_ep_dispatch(self.handle, ctypes.byref(self.dargs), self.results, stream)
+        if st:
+            raise RuntimeError(f"moe_ep_dispatch: {st} {self.lib.moe_ep_last_error().decode()}")
+
+    def combine(self, stream):
+        st = self.lib.moe_ep_combine(self.handle, ctypes.byref(self.cargs), stream)
+        if st:
+            raise RuntimeError(f"moe_ep_combine: {st} {self.lib.moe_ep_last_error().decode()}")
+
+
+def expert_standin_torch(w, d, res, values, tpr, out):
+    """The caller's expert computation, stood in for: on rank d, row r of a
+    routed token (s, t) = value(s, t) x (weights of its experts that rank d
+    owns); rows holding no token are NaN.  Untimed."""
+    import torch
+    epr = w.num_experts // w.ep_size
+    ids = res.topk_ids.long()
+    wts = res.topk_weights
+    local = (ids >= d * epr) & (ids < (d + 1) * epr)
+    wsum = (wts * local.float()).sum(dim=1)
+    rows = w.ep_size * tpr
+    full = torch.zeros((rows, w.hidden_size), dtype=torch.float32, device=out.device)
+    for s in range(w.ep_size):
+        n = values[s].shape[0]
+        if n:
+            full[s * tpr:s * tpr + n] = values[s]
+    full = full * wsum[:, None]
+    valid = ids[:, 0] != -1
+    full[~valid] = float("nan")
+    out.copy_(full.to(out.dtype))
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline
+# ---------------------------------------------------------------------------
+def cpu_baseline(w, inp, bytes_per_round, seconds):
+    import oracle
+    p = oracle.Params(w.ep_size, w.num_experts, w.top_k, w.max_tokens_per_rank, w.hidden_size,
+                      w.hidden_row_bytes, w.scale_row_bytes, -1, inp.active_rank_mask is not None)
+    spent = 0.0
+    rounds = 0
+    while spent < seconds:
+        om = oracle.OracleMoEEp(p)
+        t0 = time.perf_counter()
+        res = om.dispatch(inp.hidden, inp.topk_ids, inp.topk_weights, hidden_states_scale=inp.scale,
+                          runtime_max_tokens_per_rank=inp.runtime_max_tokens_per_rank,
+                          active_rank_mask=inp.active_rank_mask)
+        t1 = time.perf_counter()
+        if rounds == 0:
+            eo = oracle.expert_standin(p, res, inp.values, w.combine_dtype)
+        t2 = time.perf_counter()
+        om.combine(eo, w.combine_dtype, active_rank_mask=inp.active_rank_mask)
+        t3 = time.perf_counter()
+        spent += (t1 - t0) + (t3 - t2)
+        rounds += 1
+    gbs = bytes_per_round * rounds / spent / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rounds} full {w.name} rounds (dispatch+combine, stand-in excluded), "
+                      f"{spent:.1f} s, single-threaded NumPy",
+            "us_per_round": round(spent / rounds * 1e6, 1),
+            "host_cpus": os.cpu_count(), "host_affinity": len(os.sched_getaffinity(0))}
+
+
+def kernel_source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed PMC summary, if it
+    was taken on the current kernel source; else None."""
+    path = TRAFFIC_FILE.format(workload=workload)
+    if not os.path.exists(path):
+        return None
+    src_hash = None
+    val = None
+    for line in open(path):
+        parts = line.split()
+        if len(parts) >= 2 and parts[0] == "kernel_source_sha256:":
+            src_hash = parts[1]
+        if len(parts) >= 3 and parts[0] == "traffic_bytes_per_launch:" and parts[1] == kernel:
+            val = float(parts[2])
+    if src_hash != kernel_source_hash():
+        return None
+    return val
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--instances", type=int, default=4)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also time a plain 1 GiB device-to-device copy (for the PMC byte scale)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (the EP group's ranks are partitions of one GPU's HBM); "
+              f"--gpus {args.gpus} / WORLD_SIZE {world} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from synth import workloads as wl
+    from combine_token_dest_amd import _lib
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    _lib.load()
+    if not _lib.moe_ep_is_platform_supported():
+        print("not a gfx950 device", file=sys.stderr)
+        sys.exit(1)
+    device = torch.device("cuda", 0)
+    torch.cuda.set_device(device)
+
+    w = wl.BY_NAME[args.workload]
+    log(f"[bench] workload {w.name} seed {w.seed}: generating inputs")
+    inp = wl.make_inputs(w)
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    dev_hidden = [to(h) for h in inp.hidden]
+    dev_ids = [to(i) for i in inp.topk_ids]
+    dev_w = [to(x) for x in inp.topk_weights]
+    dev_s = [to(x) for x in inp.scale] if inp.scale is not None else None
+    dev_vals = [to(v) for v in inp.values]
+    dev_inputs = (dev_hidden, dev_ids, dev_w, dev_s, dev_vals)
+
+    log(f"[bench] building {args.instances} instances")
+    insts = [Instance(w, inp, dev_inputs, device) for _ in range(args.instances)]
+    del dev_vals
+    torch.cuda.synchronize()
+    tpr = insts[0].tpr
+    masks = destination_masks(w, inp)
+    b_d, b_c, N, P, R = algorithmic_bytes(w, inp.local_num_tokens, masks, tpr, True)
+    bytes_round = b_d + b_c
+
+    stream = torch.cuda.current_stream(device)
+    sp = stream.cuda_stream
+    I = len(insts)
+
+    log(f"[bench] warmup {args.warmup}")
+    for i in range(args.warmup):
+        insts[i % I].dispatch(sp)
+        insts[i % I].combine(sp)
+    torch.cuda.synchronize()
+
+    # Timed region: K steps, HIP events around every launch on the launch stream.
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    log(f"[bench] timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        inst = insts[i % I]
+        e = ev[i]
+        e[0].record(stream)
+        inst.dispatch(sp)
+        e[1].record(stream)
+        inst.combine(sp)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_s = t1 - t0
+    d_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
+    c_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
+
+    # Same steps without events, for the event overhead on the step time.
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(K):
+        insts[i % I].dispatch(sp)
+        insts[i % I].combine(sp)
+    torch.cuda.synchronize()
+    wall_plain = time.perf_counter() - t2
+
+    ms_step = wall_s / K * 1e3
+    value = bytes_round / (wall_s / K) / 1e9
+    d_us, c_us = d_ms.mean() * 1e3, c_ms.mean() * 1e3
+    d_gbs, c_gbs = b_d / (d_us * 1e-6) / 1e9, b_c / (c_us * 1e-6) / 1e9
+    dominant = "dispatch_kernel" if d_us >= c_us else "combine_kernel"
+    dom_bytes, dom_us, dom_gbs = (b_d, d_us, d_gbs) if dominant == "dispatch_kernel" else (b_c, c_us, c_gbs)
+    traffic = read_traffic(w.name, dominant)
+
+    copy_info = None
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=device)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        copy_info = {"bytes": 2 * (1 << 30), "ms": round(ms, 4), "GB/s": round(2 * (1 << 30) / ms / 1e6, 1)}
+        del src, dst
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline, ~{args.cpu_seconds:.0f} s")
+        cpu = cpu_baseline(w, inp, bytes_round, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "payload_dtype": w.row_format,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: ep_size={w.ep_size} logical ranks on 1 GPU, "
+                               f"tokens_per_rank={tpr}, hidden={w.hidden_size} {w.row_format}, "
+                               f"num_experts={w.num_experts}, top_k={w.top_k}",
+                   "ep_size": w.ep_size, "tokens_per_rank": tpr, "hidden": w.hidden_size,
+                   "num_experts": w.num_experts, "top_k": w.top_k, "row_format": w.row_format,
+                   "instances_rotated": I, "seed": w.seed},
+        "us_per_round": round(ms_step * 1e3, 2),
+        "us_per_round_kernels": round(d_us + c_us, 2),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "pct_hbm_peak_kernels": round(100 * bytes_round / ((d_us + c_us) * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+        "bytes_per_round": bytes_round,
+        "routed_pairs": P, "tokens": N, "receive_rows": R,
+        "kernels": {
+            "dispatch_kernel": {"us_mean": round(d_us, 3), "us_p10": round(float(np.percentile(d_ms, 10)) * 1e3, 3),
+                                "us_p50": round(float(np.median(d_ms)) * 1e3, 3),
+                                "us_p90": round(float(np.percentile(d_ms, 90)) * 1e3, 3),
+                                "bytes": b_d, "GB/s": round(d_gbs, 1)},
+            "combine_kernel": {"us_mean": round(c_us, 3), "us_p10": round(float(np.percentile(c_ms, 10)) * 1e3, 3),
+                               "us_p50": round(float(np.median(c_ms)) * 1e3, 3),
+                               "us_p90": round(float(np.percentile(c_ms, 90)) * 1e3, 3),
+                               "bytes": b_c, "GB/s": round(c_gbs, 1)},
+        },
+        "us_per_round_no_events": round(wall_plain / K * 1e6, 2),
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": dom_bytes,
+                     "us_per_launch": round(dom_us, 3)},
+        "cpu_baseline": cpu,
+        "kernel_source_sha256": kernel_source_hash(),
+    }
+    if copy_info:
+        out["copy_1GiB"] = copy_info
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

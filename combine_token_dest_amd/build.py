@@ -1,0 +1,62 @@
+"""Build libmoe_ep.so (the gfx950 dispatch/combine library) in-tree with hipcc.
+
+    python -m combine_token_dest_amd.build
+
+Every call compiles from source; the library lands next to this file.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libmoe_ep.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+
+ARCH = "gfx950"
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+# -packed-fp32-ops: keep hipcc from fusing float adds into v_pk_add_f32.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall",
+          f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
+def _run(cmd):
+    proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in proc.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if proc.returncode != 0:
+        raise RuntimeError(f"build step failed ({proc.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the kernels for gfx950 and the host API, link LIB_PATH."""
+    with tempfile.TemporaryDirectory(prefix="moe_ep_build_") as tmp:
+        k_obj = os.path.join(tmp, "moe_ep_kernels.o")
+        a_obj = os.path.join(tmp, "moe_ep_api.o")
+        lib_tmp = os.path.join(tmp, LIB_NAME)
+        steps = [
+            [HIPCC, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, "-x", "hip", "-c",
+             os.path.join(CSRC, "moe_ep_kernels.hip"), "-o", k_obj],
+            [HIPCC, *COMMON, "-c", os.path.join(CSRC, "moe_ep_api.cpp"), "-o", a_obj],
+            [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", k_obj, a_obj, "-o", lib_tmp],
+        ]
+        for cmd in steps:
+            out = _run(cmd)
+            if verbose and out.strip():
+                print(out)
+        shutil.move(lib_tmp, LIB_PATH + ".tmp")
+        os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

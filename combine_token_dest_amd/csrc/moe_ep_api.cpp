@@ -1,0 +1,411 @@
+// C-ABI host side of the gfx950 rank-major MoE expert-parallel
+// dispatch/combine library: argument validation, the dispatch -> combine
+// call protocol, the workspace layout, and kernel launches.
+//
+// Everything here runs on the host before anything is enqueued, so a call
+// that fails leaves no device work behind and the handle unchanged.
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "moe_ep.h"
+#include "moe_ep_internal.h"
+
+using namespace moe_ep_detail;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  return MOE_EP_OK;
+}
+
+constexpr int64_t kAlign = 256;
+
+int64_t align_up(int64_t x, int64_t a) {
+  return (x + a - 1) / a * a;
+}
+
+enum State { kIdle = 0, kDispatched = 1 };
+
+uint64_t rank_bits(int ep) {
+  return ep >= 64 ? ~0ull : ((1ull << ep) - 1);
+}
+
+bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+// Largest power of two <= cap that divides x (x > 0).
+int64_t pow2_divisor(uint64_t x, int64_t cap) {
+  int64_t v = cap;
+  while (v > 1 && (x % (uint64_t)v) != 0) v >>= 1;
+  return v;
+}
+
+// Multiply-shift constants for e / d with 0 <= e < 2^31 (Granlund &
+// Montgomery 1994, Thm. 4.2 with N = 31): l = ceil(log2 d),
+// magic = ceil(2^(31+l) / d), shift = 31 + l.
+OwnerDiv make_owner_div(uint32_t d) {
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  const unsigned __int128 num = (unsigned __int128)1 << (31 + l);
+  const uint64_t magic = (uint64_t)((num + d - 1) / d);
+  return OwnerDiv{magic, 31 + l};
+}
+
+int validate_params(const moe_ep_params* p) {
+  if (!p) return fail(MOE_EP_ERR_INVALID_ARG, "params is NULL");
+  if (p->ep_size < 1 || p->ep_size > MOE_EP_MAX_RANKS)
+    return fail(MOE_EP_ERR_INVALID_ARG, "ep_size %d outside [1, %d]", p->ep_size, MOE_EP_MAX_RANKS);
+  if (p->num_experts < p->ep_size || p->num_experts % p->ep_size != 0)
+    return fail(MOE_EP_ERR_INVALID_ARG, "num_experts %d is not a positive multiple of ep_size %d",
+                p->num_experts, p->ep_size);
+  if (p->top_k < 1) return fail(MOE_EP_ERR_INVALID_ARG, "top_k %d < 1", p->top_k);
+  if (p->max_tokens_per_rank < 0)
+    return fail(MOE_EP_ERR_INVALID_ARG, "max_tokens_per_rank %d < 0", p->max_tokens_per_rank);
+  if (p->hidden_size < 1) return fail(MOE_EP_ERR_INVALID_ARG, "hidden_size %d < 1", p->hidden_size);
+  if (p->combine_max_elem_bytes != 2 && p->combine_max_elem_bytes != 4)
+    return fail(MOE_EP_ERR_INVALID_ARG, "combine_max_elem_bytes %d is not 2 or 4", p->combine_max_elem_bytes);
+  if (p->hidden_row_bytes < 1)
+    return fail(MOE_EP_ERR_INVALID_ARG, "hidden_row_bytes %lld < 1", (long long)p->hidden_row_bytes);
+  if (p->scale_row_bytes < 0)
+    return fail(MOE_EP_ERR_INVALID_ARG, "scale_row_bytes %lld < 0", (long long)p->scale_row_bytes);
+  // Row and grid indices are 32-bit in the kernels; byte offsets are 64-bit.
+  const int64_t rows = (int64_t)p->ep_size * p->max_tokens_per_rank;
+  if (rows > (int64_t)1 << 30) return fail(MOE_EP_ERR_INVALID_ARG, "ep_size * capacity too large");
+  if (p->hidden_row_bytes > ((int64_t)1 << 31) || p->scale_row_bytes > ((int64_t)1 << 31))
+    return fail(MOE_EP_ERR_INVALID_ARG, "row bytes too large");
+  return ok();
+}
+
+// Partition layout; returns false on overflow.
+bool make_layout(const moe_ep_params* p, Layout* L) {
+  const unsigned __int128 rows = (unsigned __int128)p->ep_size * (unsigned __int128)p->max_tokens_per_rank;
+  const unsigned __int128 hid = rows * (unsigned __int128)p->hidden_row_bytes;
+  const unsigned __int128 scl = rows * (unsigned __int128)p->scale_row_bytes;
+  const unsigned __int128 ids = rows * (unsigned __int128)p->top_k * 4;
+  const unsigned __int128 cmb = rows * (unsigned __int128)p->hidden_size * (unsigned __int128)p->combine_max_elem_bytes;
+  const unsigned __int128 limit = (unsigned __int128)1 << 62;
+  if (hid > limit || scl > limit || ids > limit || cmb > limit) return false;
+  int64_t off = 0;
+  L->off_hidden = off;
+  off += align_up((int64_t)hid, kAlign);
+  L->off_scale = off;
+  off += align_up((int64_t)scl, kAlign);
+  L->off_ids = off;
+  off += align_up((int64_t)ids, kAlign);
+  L->off_weights = off;
+  off += align_up((int64_t)ids, kAlign);
+  L->off_combine = off;
+  off += align_up((int64_t)cmb, kAlign);
+  L->part_stride = align_up(off, 4096);
+  const unsigned __int128 parts = (unsigned __int128)L->part_stride * (unsigned __int128)p->ep_size;
+  if (parts > limit) return false;
+  L->off_route = (int64_t)parts;
+  const unsigned __int128 total = parts + (unsigned __int128)align_up((int64_t)(rows * 8), kAlign);
+  if (total > limit) return false;
+  L->total = total > 0 ? (int64_t)total : kAlign;   // never a zero-byte workspace
+  return true;
+}
+
+}  // namespace
+
+struct moe_ep_handle_s {
+  moe_ep_params p;
+  Layout L;
+  uint8_t* ws;
+  OwnerDiv owner;
+  int state;
+  // Remembered from the dispatch for its combine.
+  int32_t tpr;
+  int32_t n[MOE_EP_MAX_RANKS];
+  uint64_t mask;       // as passed (MOE_EP_ALL_RANKS = none)
+};
+
+extern "C" {
+
+const char* moe_ep_status_string(int status) {
+  switch (status) {
+    case MOE_EP_OK: return "MOE_EP_OK";
+    case MOE_EP_ERR_INVALID_ARG: return "MOE_EP_ERR_INVALID_ARG";
+    case MOE_EP_ERR_STATE: return "MOE_EP_ERR_STATE";
+    case MOE_EP_ERR_CAPACITY: return "MOE_EP_ERR_CAPACITY";
+    case MOE_EP_ERR_MASK: return "MOE_EP_ERR_MASK";
+    case MOE_EP_ERR_ALIGN: return "MOE_EP_ERR_ALIGN";
+    case MOE_EP_ERR_HIP: return "MOE_EP_ERR_HIP";
+    case MOE_EP_ERR_UNSUPPORTED: return "MOE_EP_ERR_UNSUPPORTED";
+    default: return "MOE_EP_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_ep_last_error(void) {
+  return g_last_error.c_str();
+}
+
+int moe_ep_is_platform_supported(void) {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count < 1) return 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+  return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+}
+
+int moe_ep_workspace_bytes(const moe_ep_params* params, size_t* out_bytes) {
+  if (!out_bytes) return fail(MOE_EP_ERR_INVALID_ARG, "out_bytes is NULL");
+  const int st = validate_params(params);
+  if (st != MOE_EP_OK) return st;
+  Layout L;
+  if (!make_layout(params, &L)) return fail(MOE_EP_ERR_INVALID_ARG, "workspace size overflows");
+  *out_bytes = (size_t)L.total;
+  return ok();
+}
+
+int moe_ep_create(const moe_ep_params* params, void* workspace, size_t workspace_bytes,
+                  moe_ep_handle* out_handle) {
+  if (!out_handle) return fail(MOE_EP_ERR_INVALID_ARG, "out_handle is NULL");
+  const int st = validate_params(params);
+  if (st != MOE_EP_OK) return st;
+  Layout L;
+  if (!make_layout(params, &L)) return fail(MOE_EP_ERR_INVALID_ARG, "workspace size overflows");
+  if (!workspace) return fail(MOE_EP_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned(workspace, kAlign)) return fail(MOE_EP_ERR_ALIGN, "workspace is not 256-byte aligned");
+  if (workspace_bytes < (size_t)L.total)
+    return fail(MOE_EP_ERR_INVALID_ARG, "workspace has %zu bytes, needs %lld", workspace_bytes,
+                (long long)L.total);
+  moe_ep_handle h = new (std::nothrow) moe_ep_handle_s();
+  if (!h) return fail(MOE_EP_ERR_INVALID_ARG, "out of host memory");
+  h->p = *params;
+  h->L = L;
+  h->ws = static_cast<uint8_t*>(workspace);
+  h->owner = make_owner_div((uint32_t)(params->num_experts / params->ep_size));
+  h->state = kIdle;
+  h->tpr = 0;
+  h->mask = MOE_EP_ALL_RANKS;
+  *out_handle = h;
+  return ok();
+}
+
+int moe_ep_destroy(moe_ep_handle handle) {
+  delete handle;
+  return ok();
+}
+
+int moe_ep_active_rank_mask(const int32_t* ranks, int32_t n, uint64_t* out_mask) {
+  if (!out_mask) return fail(MOE_EP_ERR_INVALID_ARG, "out_mask is NULL");
+  if (n < 0 || (n > 0 && !ranks)) return fail(MOE_EP_ERR_INVALID_ARG, "bad rank list");
+  uint64_t m = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (ranks[i] < 0 || ranks[i] >= MOE_EP_MAX_RANKS)
+      return fail(MOE_EP_ERR_MASK, "rank %d outside [0, %d)", ranks[i], MOE_EP_MAX_RANKS);
+    m |= 1ull << ranks[i];
+  }
+  *out_mask = m;
+  return ok();
+}
+
+static int check_mask(const moe_ep_params& p, uint64_t mask) {
+  if (mask == MOE_EP_ALL_RANKS) return MOE_EP_OK;
+  if (!p.enable_rank_mask) return fail(MOE_EP_ERR_MASK, "active_rank_mask passed without enable_rank_mask");
+  if (mask & ~rank_bits(p.ep_size))
+    return fail(MOE_EP_ERR_MASK, "active_rank_mask 0x%llx has bits at or above ep_size %d",
+                (unsigned long long)mask, p.ep_size);
+  return MOE_EP_OK;
+}
+
+int moe_ep_dispatch(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispatch_result* results,
+                    void* stream) {
+  if (!h || !a || !results) return fail(MOE_EP_ERR_INVALID_ARG, "NULL handle, args or results");
+  const moe_ep_params& p = h->p;
+  const int ep = p.ep_size;
+  if (h->state != kIdle) return fail(MOE_EP_ERR_STATE, "dispatch called before the previous dispatch's combine");
+
+  int32_t largest = 0;
+  for (int s = 0; s < ep; ++s) {
+    const int32_t n = a->local_num_tokens[s];
+    if (n < 0) return fail(MOE_EP_ERR_INVALID_ARG, "rank %d: local_num_tokens %d < 0", s, n);
+    if (n > p.max_tokens_per_rank)
+      return fail(MOE_EP_ERR_CAPACITY, "rank %d: local_num_tokens %d > capacity %d", s, n,
+                  p.max_tokens_per_rank);
+    if (n > largest) largest = n;
+  }
+  const int32_t tpr = a->runtime_max_tokens_per_rank < 0 ? p.max_tokens_per_rank : a->runtime_max_tokens_per_rank;
+  if (tpr > p.max_tokens_per_rank)
+    return fail(MOE_EP_ERR_CAPACITY, "runtime_max_tokens_per_rank %d > capacity %d", tpr, p.max_tokens_per_rank);
+  if (tpr < largest)
+    return fail(MOE_EP_ERR_CAPACITY, "runtime_max_tokens_per_rank %d < largest local_num_tokens %d", tpr,
+                largest);
+  int st = check_mask(p, a->active_rank_mask);
+  if (st != MOE_EP_OK) return st;
+
+  const uint64_t all = rank_bits(ep);
+  const uint64_t wp = a->weights_present & all;
+  const uint64_t sp = a->scales_present & all;
+  if (wp != 0 && wp != all)
+    return fail(MOE_EP_ERR_INVALID_ARG, "topk_weights passed by some ranks only (mask 0x%llx)",
+                (unsigned long long)wp);
+  if (sp != 0 && sp != all)
+    return fail(MOE_EP_ERR_INVALID_ARG, "hidden_states_scale passed by some ranks only (mask 0x%llx)",
+                (unsigned long long)sp);
+  const bool has_w = wp != 0;
+  const bool has_s = sp != 0;
+  if (has_s && p.scale_row_bytes == 0)
+    return fail(MOE_EP_ERR_INVALID_ARG, "hidden_states_scale passed but scale_row_bytes is 0");
+
+  DispatchKArgs k;
+  std::memset(&k, 0, sizeof(k));
+  uint64_t hidden_align_or = (uint64_t)p.hidden_row_bytes;
+  uint64_t scale_align_or = has_s ? (uint64_t)p.scale_row_bytes : 0;
+  for (int s = 0; s < ep; ++s) {
+    const int32_t n = a->local_num_tokens[s];
+    k.n[s] = n;
+    if (n == 0) continue;
+    if (!a->hidden[s] || !a->topk_ids[s])
+      return fail(MOE_EP_ERR_INVALID_ARG, "rank %d: NULL hidden or topk_ids with %d tokens", s, n);
+    if (!aligned(a->topk_ids[s], 4)) return fail(MOE_EP_ERR_ALIGN, "rank %d: topk_ids not 4-byte aligned", s);
+    if (has_w) {
+      if (!a->topk_weights[s]) return fail(MOE_EP_ERR_INVALID_ARG, "rank %d: NULL topk_weights", s);
+      if (!aligned(a->topk_weights[s], 4))
+        return fail(MOE_EP_ERR_ALIGN, "rank %d: topk_weights not 4-byte aligned", s);
+    }
+    if (has_s) {
+      if (!a->hidden_scale[s]) return fail(MOE_EP_ERR_INVALID_ARG, "rank %d: NULL hidden_states_scale", s);
+      scale_align_or |= reinterpret_cast<uintptr_t>(a->hidden_scale[s]);
+    }
+    hidden_align_or |= reinterpret_cast<uintptr_t>(a->hidden[s]);
+    k.hidden[s] = static_cast<const uint8_t*>(a->hidden[s]);
+    k.ids[s] = a->topk_ids[s];
+    k.weights[s] = has_w ? a->topk_weights[s] : nullptr;
+    k.scale[s] = has_s ? static_cast<const uint8_t*>(a->hidden_scale[s]) : nullptr;
+  }
+  const int vec_bytes = (int)pow2_divisor(hidden_align_or, 16);
+
+  k.ws = h->ws;
+  k.route = reinterpret_cast<uint64_t*>(h->ws + h->L.off_route);
+  k.part_stride = h->L.part_stride;
+  k.off_hidden = h->L.off_hidden;
+  k.off_scale = h->L.off_scale;
+  k.off_ids = h->L.off_ids;
+  k.off_weights = h->L.off_weights;
+  k.hidden_bytes = p.hidden_row_bytes;
+  k.scale_bytes = has_s ? p.scale_row_bytes : 0;
+  k.scale_vec4 = has_s && (scale_align_or % 4 == 0);
+  k.active = (a->active_rank_mask == MOE_EP_ALL_RANKS ? ~0ull : a->active_rank_mask) & all;
+  k.owner = h->owner;
+  k.num_experts = p.num_experts;
+  k.top_k = p.top_k;
+  k.ep = ep;
+  k.tpr = tpr;
+  k.invalid_id = p.invalid_expert_id;
+  k.has_weights = has_w ? 1 : 0;
+
+  const hipError_t e = launch_dispatch(k, vec_bytes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MOE_EP_ERR_HIP, "dispatch launch failed: %s", hipGetErrorString(e));
+
+  h->state = kDispatched;
+  h->tpr = tpr;
+  for (int s = 0; s < MOE_EP_MAX_RANKS; ++s) h->n[s] = s < ep ? a->local_num_tokens[s] : 0;
+  h->mask = a->active_rank_mask;
+  for (int d = 0; d < ep; ++d) {
+    uint8_t* part = h->ws + (int64_t)d * h->L.part_stride;
+    results[d].hidden = part + h->L.off_hidden;
+    results[d].hidden_scale = has_s ? part + h->L.off_scale : nullptr;
+    results[d].topk_ids = reinterpret_cast<int32_t*>(part + h->L.off_ids);
+    results[d].topk_weights = has_w ? reinterpret_cast<float*>(part + h->L.off_weights) : nullptr;
+    results[d].tokens_per_rank = tpr;
+    results[d].num_rows = ep * tpr;
+  }
+  return ok();
+}
+
+int moe_ep_get_combine_input_buffer(moe_ep_handle h, int32_t rank, int32_t dtype, void** out_ptr) {
+  if (!h || !out_ptr) return fail(MOE_EP_ERR_INVALID_ARG, "NULL handle or out_ptr");
+  if (h->state != kDispatched)
+    return fail(MOE_EP_ERR_STATE, "the combine input buffer is valid only between dispatch and combine");
+  if (rank < 0 || rank >= h->p.ep_size) return fail(MOE_EP_ERR_INVALID_ARG, "rank %d outside [0, %d)", rank, h->p.ep_size);
+  const int esz = dtype == MOE_EP_F32 ? 4 : dtype == MOE_EP_BF16 ? 2 : 0;
+  if (esz == 0) return fail(MOE_EP_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (esz > h->p.combine_max_elem_bytes)
+    return fail(MOE_EP_ERR_INVALID_ARG, "dtype of %d bytes exceeds combine_max_elem_bytes %d", esz,
+                h->p.combine_max_elem_bytes);
+  *out_ptr = h->ws + (int64_t)rank * h->L.part_stride + h->L.off_combine;
+  return ok();
+}
+
+int moe_ep_combine(moe_ep_handle h, const moe_ep_combine_args* a, void* stream) {
+  if (!h || !a) return fail(MOE_EP_ERR_INVALID_ARG, "NULL handle or args");
+  const moe_ep_params& p = h->p;
+  const int ep = p.ep_size;
+  if (h->state != kDispatched) return fail(MOE_EP_ERR_STATE, "combine called without a preceding dispatch");
+  int st = check_mask(p, a->active_rank_mask);
+  if (st != MOE_EP_OK) return st;
+  if (a->active_rank_mask != h->mask)
+    return fail(MOE_EP_ERR_MASK, "combine active_rank_mask 0x%llx differs from dispatch's 0x%llx",
+                (unsigned long long)a->active_rank_mask, (unsigned long long)h->mask);
+  const int esz = a->dtype == MOE_EP_F32 ? 4 : a->dtype == MOE_EP_BF16 ? 2 : 0;
+  if (esz == 0) return fail(MOE_EP_ERR_INVALID_ARG, "unknown dtype %d", a->dtype);
+
+  const uint64_t active = (h->mask == MOE_EP_ALL_RANKS ? ~0ull : h->mask) & rank_bits(ep);
+  CombineKArgs k;
+  std::memset(&k, 0, sizeof(k));
+  uint64_t align_or = (uint64_t)p.hidden_size * esz;
+  for (int d = 0; d < ep; ++d) {
+    const uint8_t* src = static_cast<const uint8_t*>(a->expert_output[d]);
+    if (!((active >> d) & 1)) {      // masked-off ranks are never read
+      k.expert_output[d] = nullptr;
+      continue;
+    }
+    if (!src) {
+      if (esz > p.combine_max_elem_bytes)
+        return fail(MOE_EP_ERR_INVALID_ARG, "rank %d: the combine input buffer holds %d-byte elements at most",
+                    d, p.combine_max_elem_bytes);
+      src = h->ws + (int64_t)d * h->L.part_stride + h->L.off_combine;
+    }
+    if (!aligned(src, esz)) return fail(MOE_EP_ERR_ALIGN, "rank %d: expert_output not element-aligned", d);
+    align_or |= reinterpret_cast<uintptr_t>(src);
+    k.expert_output[d] = src;
+  }
+  int32_t total = 0;
+  for (int s = 0; s < ep; ++s) {
+    k.token_start[s] = total;
+    const int32_t n = h->n[s];
+    total += n;
+    if (n == 0) continue;
+    if (!a->output[s]) return fail(MOE_EP_ERR_INVALID_ARG, "rank %d: NULL output with %d tokens", s, n);
+    if (!aligned(a->output[s], esz)) return fail(MOE_EP_ERR_ALIGN, "rank %d: output not element-aligned", s);
+    align_or |= reinterpret_cast<uintptr_t>(a->output[s]);
+    k.output[s] = static_cast<uint8_t*>(a->output[s]);
+  }
+  k.token_start[ep] = total;
+  const int vec_elems = (int)(pow2_divisor(align_or, 16) / esz);
+  k.route = reinterpret_cast<const uint64_t*>(h->ws + h->L.off_route);
+  k.hidden = p.hidden_size;
+  k.tpr = h->tpr;
+  k.ep = ep;
+
+  const hipError_t e = launch_combine(k, a->dtype, vec_elems < 1 ? 1 : vec_elems, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MOE_EP_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));
+  h->state = kIdle;
+  return ok();
+}
+
+}  // extern "C"

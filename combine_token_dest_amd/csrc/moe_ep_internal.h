@@ -1,0 +1,88 @@
+// Internal interface between the C-ABI host code (moe_ep_api.cpp) and the
+// gfx950 kernels (moe_ep_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "moe_ep.h"
+
+namespace moe_ep_detail {
+
+constexpr int kMaxRanks = MOE_EP_MAX_RANKS;
+
+// Byte offsets of one rank's partition of the workspace.  Partition d starts
+// at d * part_stride; the per-token destination masks follow the last one.
+struct Layout {
+  int64_t off_hidden;    // [ep*cap, hidden_row_bytes]
+  int64_t off_scale;     // [ep*cap, scale_row_bytes]
+  int64_t off_ids;       // [ep*cap, top_k] int32
+  int64_t off_weights;   // [ep*cap, top_k] float
+  int64_t off_combine;   // [ep*cap, hidden_size * combine_max_elem_bytes]
+  int64_t part_stride;   // bytes per rank partition
+  int64_t off_route;     // [ep, cap] uint64 destination masks
+  int64_t total;         // workspace bytes
+};
+
+// Exact division of expert ids by experts-per-rank with a multiply and a
+// shift (Granlund & Montgomery, "Division by invariant integers using
+// multiplication", 1994, Thm. 4.2, with N = 31): for 0 <= e < 2^31,
+// e / epr == (e * magic) >> shift.
+struct OwnerDiv {
+  uint64_t magic;
+  uint32_t shift;
+};
+
+// Kernel arguments of the dispatch kernel, passed by value.
+struct DispatchKArgs {
+  const uint8_t* hidden[kMaxRanks];    // per source rank
+  const uint8_t* scale[kMaxRanks];
+  const int32_t* ids[kMaxRanks];
+  const float* weights[kMaxRanks];
+  int32_t n[kMaxRanks];                // local_num_tokens
+  uint8_t* ws;                         // workspace base
+  uint64_t* route;                     // [ep, tpr] destination masks (inside ws)
+  int64_t part_stride;
+  int64_t off_hidden, off_scale, off_ids, off_weights;
+  int64_t hidden_bytes;                // H
+  int64_t scale_bytes;                 // S (0 when no scales are forwarded)
+  uint64_t active;                     // active ranks & ((1 << ep) - 1)
+  OwnerDiv owner;
+  int32_t num_experts;
+  int32_t top_k;
+  int32_t ep;
+  int32_t tpr;
+  int32_t invalid_id;
+  int32_t has_weights;
+  int32_t scale_vec4;                  // scale rows copied as 4-byte words (else bytes)
+};
+
+// Kernel arguments of the combine kernel, passed by value.
+struct CombineKArgs {
+  const uint8_t* expert_output[kMaxRanks];  // per rank d: [ep*tpr, hidden]
+  uint8_t* output[kMaxRanks];               // per source rank s: [n_s, hidden]
+  int32_t token_start[kMaxRanks + 1];       // prefix sums of n_s
+  const uint64_t* route;                    // [ep, tpr]
+  int64_t hidden;                           // elements per row
+  int32_t tpr;
+  int32_t ep;
+};
+
+struct LaunchShape {
+  int grid;
+  int block;
+};
+
+// Enqueue one dispatch kernel.  vec_bytes in {16, 8, 4, 2, 1} must divide
+// hidden_bytes and every hidden row pointer.
+hipError_t launch_dispatch(const DispatchKArgs& a, int vec_bytes, hipStream_t stream);
+
+// Enqueue one combine kernel over a.token_start[ep] tokens.  vec_elems must
+// divide the hidden size and every row pointer's alignment in elements.
+hipError_t launch_combine(const CombineKArgs& a, int dtype, int vec_elems, hipStream_t stream);
+
+// Launch shapes the two launchers use (exposed for tests of the host logic).
+LaunchShape dispatch_shape(int64_t rows, int64_t hidden_bytes, int vec_bytes);
+LaunchShape combine_shape(int64_t tokens, int64_t hidden, int vec_elems);
+
+}  // namespace moe_ep_detail

@@ -1,0 +1,240 @@
+"""MoEEp: the flashinfer.moe_ep API shape over the gfx950 library, one
+process holding all ep_size ranks of a group.
+
+Per-rank arguments of the pages' API become lists indexed by rank.  torch is
+used for device memory (the workspace, output tensors) and for the current
+stream only; every step of dispatch and combine runs in libmoe_ep.so.
+
+Sources: flashinfer.moe_ep.MoEEpCommunication (class description,
+is_platform_supported(), dispatch(), combine(), get_combine_input_buffer(),
+destroy()); flashinfer.moe_ep.NVLinkOneSidedAlltoAll (active_rank_mask(), the
+mask notes of dispatch() and combine()).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import MOE_EP_ALL_RANKS, MOE_EP_BF16, MOE_EP_F32
+
+_COMBINE_DTYPES = {torch.float32: MOE_EP_F32, torch.bfloat16: MOE_EP_BF16}
+
+
+@dataclass
+class DispatchResult:
+    """What one destination rank received (views into the workspace, valid
+    until the next dispatch)."""
+
+    hidden: torch.Tensor                    # [ep*tpr, hidden_row_bytes / itemsize] of the hidden dtype
+    hidden_scale: Optional[torch.Tensor]    # [ep*tpr, scale_row_bytes / itemsize] or None
+    topk_ids: torch.Tensor                  # int32 [ep*tpr, top_k]
+    topk_weights: Optional[torch.Tensor]    # float32 [ep*tpr, top_k] or None
+    tokens_per_rank: int
+
+
+def _mask_value(mask) -> int:
+    if mask is None:
+        return MOE_EP_ALL_RANKS
+    if isinstance(mask, torch.Tensor):
+        if mask.device.type != "cpu" or mask.numel() != 1:
+            raise ValueError("active_rank_mask must be a one-element CPU tensor")
+        return int(mask.item()) & MOE_EP_ALL_RANKS
+    return int(mask) & MOE_EP_ALL_RANKS
+
+
+def _dev_ptr(t: torch.Tensor, device: torch.device, what: str) -> int:
+    if t.device != device:
+        raise ValueError(f"{what} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t.data_ptr()
+
+
+class MoEEp:
+    """One EP group of ``ep_size`` logical ranks on one GPU."""
+
+    def __init__(self, ep_size: int, num_experts: int, top_k: int, max_tokens_per_rank: int,
+                 hidden_size: int, *, hidden_row_bytes: Optional[int] = None, scale_row_bytes: int = 0,
+                 combine_max_elem_bytes: int = 2, invalid_expert_id: int = -1,
+                 enable_rank_mask: bool = False, device=None):
+        dev = torch.device("cuda") if device is None else torch.device(device)
+        if dev.type != "cuda":
+            raise ValueError(f"MoEEp needs a GPU device, got {dev}")
+        self.device = dev if dev.index is not None else torch.device("cuda", torch.cuda.current_device())
+        self.params = _lib.moe_ep_params(
+            ep_size=ep_size, num_experts=num_experts, top_k=top_k,
+            max_tokens_per_rank=max_tokens_per_rank, hidden_size=hidden_size,
+            combine_max_elem_bytes=combine_max_elem_bytes,
+            hidden_row_bytes=hidden_row_bytes if hidden_row_bytes is not None else hidden_size * 2,
+            scale_row_bytes=scale_row_bytes, invalid_expert_id=invalid_expert_id,
+            enable_rank_mask=1 if enable_rank_mask else 0)
+        nbytes = _lib.moe_ep_workspace_bytes(self.params)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        self._handle = _lib.moe_ep_create(self.params, self.workspace.data_ptr(), nbytes)
+        self._ws_base = self.workspace.data_ptr()
+        self._tpr = None
+        self._n = None
+        self._hidden_dtype = None
+        self._scale_dtype = None
+
+    # -- pages' API --------------------------------------------------------
+    @classmethod
+    def is_platform_supported(cls) -> bool:
+        """Whether the current device is a gfx950 GPU; no collective work."""
+        return _lib.moe_ep_is_platform_supported()
+
+    @staticmethod
+    def active_rank_mask(active_ranks: Sequence[int]) -> torch.Tensor:
+        """CPU uint64 bitmask of the active ranks."""
+        return torch.tensor(_lib.moe_ep_active_rank_mask(list(active_ranks)), dtype=torch.uint64)
+
+    @property
+    def ep_size(self) -> int:
+        return self.params.ep_size
+
+    def _view(self, ptr: int, rows: int, row_bytes: int, dtype: torch.dtype) -> torch.Tensor:
+        off = ptr - self._ws_base
+        flat = self.workspace[off:off + rows * row_bytes]
+        item = torch.empty((), dtype=dtype).element_size()
+        return flat.view(dtype).view(rows, row_bytes // item)
+
+    def dispatch(self, hidden_states: Sequence[torch.Tensor], topk_ids: Sequence[torch.Tensor],
+                 topk_weights: Optional[Sequence[Optional[torch.Tensor]]] = None, *,
+                 hidden_states_scale: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                 runtime_max_tokens_per_rank: Optional[int] = None,
+                 eplb_local_stats=None, active_rank_mask=None) -> List[DispatchResult]:
+        """Send every token to the ranks owning its experts; see
+        include/moe_ep.h, moe_ep_dispatch."""
+        if eplb_local_stats is not None:
+            raise NotImplementedError("eplb_local_stats is not supported by this backend")
+        if self._handle is None:
+            raise RuntimeError("MoEEp has been destroyed")
+        p = self.params
+        ep = p.ep_size
+        if len(hidden_states) != ep or len(topk_ids) != ep:
+            raise ValueError(f"expected {ep} per-rank hidden_states and topk_ids")
+        a = _lib.moe_ep_dispatch_args()
+        wp = sp = 0
+        n = []
+        for s in range(ep):
+            h, ids = hidden_states[s], topk_ids[s]
+            if ids.dtype != torch.int32:
+                raise TypeError("topk_ids must be int32")
+            if ids.dim() != 2 or ids.shape[1] != p.top_k:
+                raise ValueError(f"rank {s}: topk_ids must be [n, {p.top_k}]")
+            ns = ids.shape[0]
+            if h.shape[0] != ns or h.numel() * h.element_size() != ns * p.hidden_row_bytes:
+                raise ValueError(f"rank {s}: hidden_states must be {ns} rows of {p.hidden_row_bytes} bytes")
+            n.append(ns)
+            a.local_num_tokens[s] = ns
+            a.hidden[s] = _dev_ptr(h, self.device, f"hidden_states[{s}]") if ns else None
+            a.topk_ids[s] = _dev_ptr(ids, self.device, f"topk_ids[{s}]") if ns else None
+            if topk_weights is not None and topk_weights[s] is not None:
+                w = topk_weights[s]
+                if w.dtype != torch.float32 or tuple(w.shape) != (ns, p.top_k):
+                    raise ValueError(f"rank {s}: topk_weights must be float32 [{ns}, {p.top_k}]")
+                wp |= 1 << s
+                a.topk_weights[s] = _dev_ptr(w, self.device, f"topk_weights[{s}]") if ns else None
+            if hidden_states_scale is not None and hidden_states_scale[s] is not None:
+                sc = hidden_states_scale[s]
+                if sc.shape[0] != ns or sc.numel() * sc.element_size() != ns * p.scale_row_bytes:
+                    raise ValueError(f"rank {s}: hidden_states_scale must be {ns} rows of "
+                                     f"{p.scale_row_bytes} bytes")
+                sp |= 1 << s
+                a.hidden_scale[s] = _dev_ptr(sc, self.device, f"hidden_states_scale[{s}]") if ns else None
+        a.weights_present = wp
+        a.scales_present = sp
+        a.runtime_max_tokens_per_rank = -1 if runtime_max_tokens_per_rank is None \
+            else int(runtime_max_tokens_per_rank)
+        a.active_rank_mask = _mask_value(active_rank_mask)
+        stream = torch.cuda.current_stream(self.device).cuda_stream
+        res = _lib.moe_ep_dispatch(self._handle, a, ep, stream)
+        self._tpr = res[0].tokens_per_rank if ep else 0
+        self._n = n
+        hdt = hidden_states[0].dtype
+        sdt = None
+        if sp:
+            sdt = next(x for x in hidden_states_scale if x is not None).dtype
+        out = []
+        for d in range(ep):
+            r = res[d]
+            rows = r.num_rows
+            out.append(DispatchResult(
+                hidden=self._view(r.hidden, rows, p.hidden_row_bytes, hdt),
+                hidden_scale=self._view(r.hidden_scale, rows, p.scale_row_bytes, sdt) if r.hidden_scale else None,
+                topk_ids=self._view(r.topk_ids, rows, p.top_k * 4, torch.int32),
+                topk_weights=self._view(r.topk_weights, rows, p.top_k * 4, torch.float32)
+                if r.topk_weights else None,
+                tokens_per_rank=r.tokens_per_rank))
+        return out
+
+    def get_combine_input_buffer(self, rank: int, dtype: torch.dtype) -> torch.Tensor:
+        """Rank ``rank``'s ``[ep*tpr, hidden]`` buffer in the workspace; valid
+        between dispatch and combine.  Passing it to combine saves a copy."""
+        if dtype not in _COMBINE_DTYPES:
+            raise TypeError(f"combine dtype must be float32 or bfloat16, got {dtype}")
+        ptr = _lib.moe_ep_get_combine_input_buffer(self._handle, rank, _COMBINE_DTYPES[dtype])
+        item = torch.empty((), dtype=dtype).element_size()
+        return self._view(ptr, self.params.ep_size * self._tpr, self.params.hidden_size * item, dtype)
+
+    def combine(self, expert_output: Sequence[Optional[torch.Tensor]], *,
+                output: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                active_rank_mask=None) -> List[torch.Tensor]:
+        """Sum every token's rows over the ranks it reached; see
+        include/moe_ep.h, moe_ep_combine.  ``expert_output[d]`` may be
+        ``[ep*tpr, hidden]`` or ``[ep, tpr, hidden]``; None means rank d's
+        combine input buffer."""
+        if self._handle is None:
+            raise RuntimeError("MoEEp has been destroyed")
+        p = self.params
+        ep = p.ep_size
+        if len(expert_output) != ep:
+            raise ValueError(f"expected {ep} per-rank expert_output tensors")
+        dtype = next((t.dtype for t in expert_output if t is not None), None)
+        if dtype is None:
+            dtype = output[0].dtype if output is not None and output[0] is not None else torch.bfloat16
+        if dtype not in _COMBINE_DTYPES:
+            raise TypeError(f"combine dtype must be float32 or bfloat16, got {dtype}")
+        if self._tpr is None:
+            raise _lib.MoeEpError(_lib.MOE_EP_ERR_STATE, "combine", "no dispatch to combine")
+        rows = ep * self._tpr
+        a = _lib.moe_ep_combine_args()
+        for d in range(ep):
+            t = expert_output[d]
+            if t is None:
+                a.expert_output[d] = None
+                continue
+            if t.dtype != dtype or t.numel() != rows * p.hidden_size:
+                raise ValueError(f"rank {d}: expert_output must be {dtype} [{rows}, {p.hidden_size}]")
+            a.expert_output[d] = _dev_ptr(t, self.device, f"expert_output[{d}]")
+        outs = []
+        for s in range(ep):
+            ns = self._n[s]
+            o = output[s] if output is not None else None
+            if o is None:
+                o = torch.empty((ns, p.hidden_size), dtype=dtype, device=self.device)
+            elif o.dtype != dtype or tuple(o.shape) != (ns, p.hidden_size):
+                raise ValueError(f"rank {s}: output must be {dtype} [{ns}, {p.hidden_size}]")
+            a.output[s] = _dev_ptr(o, self.device, f"output[{s}]") if ns else None
+            outs.append(o)
+        a.dtype = _COMBINE_DTYPES[dtype]
+        a.active_rank_mask = _mask_value(active_rank_mask)
+        stream = torch.cuda.current_stream(self.device).cuda_stream
+        _lib.moe_ep_combine(self._handle, a, stream)
+        return outs
+
+    def destroy(self) -> None:
+        """Release the handle; repeated calls do nothing."""
+        if self._handle is not None:
+            _lib.moe_ep_destroy(self._handle)
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass

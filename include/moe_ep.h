@@ -1,0 +1,196 @@
+/*
+ * moe_ep.h -- C ABI of the MI355X (gfx950) rank-major MoE expert-parallel
+ * dispatch/combine library (libmoe_ep.so).
+ *
+ * One process holds a whole expert-parallel (EP) group of ep_size logical
+ * ranks.  Each rank's receive region and combine input region is a partition
+ * of one caller-owned device workspace, so dispatch and combine are on-device
+ * scatter / gather-reduce kernels on one GPU.  Every per-rank argument of the
+ * FlashInfer API becomes an array indexed by rank.
+ *
+ * Sources of the contract (FlashInfer API pages for flashinfer.moe_ep):
+ *   MoEEpCommunication       class description, is_platform_supported(),
+ *                            dispatch(), combine(), get_combine_input_buffer(),
+ *                            destroy()
+ *   NVLinkOneSidedAlltoAll   class description (rank-major placement and
+ *                            invalid rows), active_rank_mask(), dispatch()
+ *                            (mask and weights rules), combine() (mask rule),
+ *                            get_combine_input_buffer()
+ *   CakeAlltoAll             class description (rows beyond a source's count)
+ *
+ * Conventions for every entry point:
+ *   - Pointers named "device" point to GPU memory of the current HIP device;
+ *     all other pointers are host memory and are read only during the call.
+ *   - Validation happens on the host before anything is enqueued.  On any
+ *     error no device work is queued and the handle's state is unchanged.
+ *   - Device work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) and is asynchronous: inputs must stay valid, and outputs must
+ *     not be read, until the stream has passed the call.  No entry point
+ *     synchronizes the device or allocates device memory.
+ *   - A handle serves one in-flight dispatch/combine pair and is not
+ *     thread-safe.
+ *   - Every entry point returns a moe_ep_status (0 = success) unless stated.
+ *     moe_ep_last_error() describes the most recent failure of this thread.
+ */
+#ifndef MOE_EP_H
+#define MOE_EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Symbols of this header are the library's only exports. */
+#define MOE_EP_API __attribute__((visibility("default")))
+
+/* A uint64 bitmask names the active ranks, so a group has at most 64 ranks
+ * (NVLinkOneSidedAlltoAll, active_rank_mask()). */
+#define MOE_EP_MAX_RANKS 64
+/* active_rank_mask value meaning "no mask passed": every rank is active. */
+#define MOE_EP_ALL_RANKS (~(uint64_t)0)
+
+typedef enum moe_ep_status {
+  MOE_EP_OK = 0,
+  MOE_EP_ERR_INVALID_ARG = -1,  /* bad pointer, size, dtype, or weights/scales passed by some ranks only */
+  MOE_EP_ERR_STATE = -2,        /* call out of the dispatch -> combine -> dispatch order */
+  MOE_EP_ERR_CAPACITY = -3,     /* tokens_per_rank outside [largest local count, capacity] */
+  MOE_EP_ERR_MASK = -4,         /* mask without enable_rank_mask, bits >= ep_size, or combine mask != dispatch mask */
+  MOE_EP_ERR_ALIGN = -5,        /* an int32/float/workspace pointer not aligned to its element */
+  MOE_EP_ERR_HIP = -6,          /* a HIP runtime call failed (launch or device query) */
+  MOE_EP_ERR_UNSUPPORTED = -7   /* not a gfx950 device */
+} moe_ep_status;
+
+/* Element type of combine's input and output rows (both use the same one). */
+typedef enum moe_ep_dtype {
+  MOE_EP_F32 = 0,
+  MOE_EP_BF16 = 1
+} moe_ep_dtype;
+
+/* Static sizes of one EP group (the pages' MoEEpCommParams plus the
+ * enable_rank_mask switch of the backend config). */
+typedef struct moe_ep_params {
+  int32_t ep_size;                /* ranks in the group, 1..64 */
+  int32_t num_experts;            /* global experts, a multiple of ep_size; rank d owns
+                                     experts [d*E/ep, (d+1)*E/ep) (contiguous blocks) */
+  int32_t top_k;                  /* experts per token, >= 1 */
+  int32_t max_tokens_per_rank;    /* capacity: the largest local_num_tokens of any rank */
+  int32_t hidden_size;            /* elements of a combine row */
+  int32_t combine_max_elem_bytes; /* element size the combine input buffer is sized for: 2 or 4 */
+  int64_t hidden_row_bytes;       /* bytes of one dispatched hidden_states row (opaque) */
+  int64_t scale_row_bytes;        /* bytes of one hidden_states_scale row; 0 = no scales */
+  int32_t invalid_expert_id;      /* written into every top_k slot of an invalid receive row */
+  int32_t enable_rank_mask;       /* nonzero: dispatch/combine accept an active_rank_mask */
+} moe_ep_params;
+
+/* Inputs of one dispatch, per SOURCE rank s < ep_size
+ * (MoEEpCommunication, dispatch()).  Entries at s >= ep_size are ignored. */
+typedef struct moe_ep_dispatch_args {
+  const void*    hidden[MOE_EP_MAX_RANKS];        /* device [n_s, hidden_row_bytes], rows contiguous */
+  const void*    hidden_scale[MOE_EP_MAX_RANKS];  /* device [n_s, scale_row_bytes] or NULL */
+  const int32_t* topk_ids[MOE_EP_MAX_RANKS];      /* device [n_s, top_k] global expert ids */
+  const float*   topk_weights[MOE_EP_MAX_RANKS];  /* device [n_s, top_k] or NULL */
+  int32_t        local_num_tokens[MOE_EP_MAX_RANKS]; /* n_s, 0..capacity */
+  uint64_t       weights_present;  /* bit s: rank s passed topk_weights (an empty [0, top_k]
+                                      tensor counts).  Must be none or all ranks. */
+  uint64_t       scales_present;   /* bit s: rank s passed hidden_states_scale.  None or all. */
+  int32_t        runtime_max_tokens_per_rank; /* < 0 = None = capacity; else in [max n_s, capacity] */
+  uint64_t       active_rank_mask; /* MOE_EP_ALL_RANKS = no mask; else needs enable_rank_mask
+                                      and only bits < ep_size */
+} moe_ep_dispatch_args;
+
+/* What destination rank d received: views into its workspace partition,
+ * valid until the next moe_ep_dispatch on the handle. */
+typedef struct moe_ep_dispatch_result {
+  void*    hidden;          /* device [num_rows, hidden_row_bytes] */
+  void*    hidden_scale;    /* device [num_rows, scale_row_bytes], NULL when no scales passed */
+  int32_t* topk_ids;        /* device [num_rows, top_k] */
+  float*   topk_weights;    /* device [num_rows, top_k], NULL when no weights passed */
+  int32_t  tokens_per_rank; /* tpr of this step */
+  int32_t  num_rows;        /* ep_size * tokens_per_rank */
+} moe_ep_dispatch_result;
+
+/* Inputs of one combine (MoEEpCommunication, combine()). */
+typedef struct moe_ep_combine_args {
+  const void* expert_output[MOE_EP_MAX_RANKS]; /* per rank d: device [ep*tpr, hidden_size] (the same
+                                                  memory as [ep, tpr, hidden_size]); NULL = rank d's
+                                                  combine input buffer */
+  void*       output[MOE_EP_MAX_RANKS];        /* per source rank s: device [n_s, hidden_size] */
+  int32_t     dtype;                           /* moe_ep_dtype of expert_output and output */
+  uint64_t    active_rank_mask;                /* must equal the dispatch's mask */
+} moe_ep_combine_args;
+
+typedef struct moe_ep_handle_s* moe_ep_handle;
+
+/* 1 when the current HIP device is a gfx950 (MI355X-class) GPU, else 0.
+ * Needs no handle and does no device work
+ * (MoEEpCommunication, is_platform_supported()). */
+MOE_EP_API int moe_ep_is_platform_supported(void);
+
+/* Bytes of device workspace a group with these params needs (receive
+ * regions, combine input regions and the per-token destination masks, for
+ * capacity-sized steps).  *out_bytes is set on success. */
+MOE_EP_API int moe_ep_workspace_bytes(const moe_ep_params* params, size_t* out_bytes);
+
+/* Creates a handle over a caller-owned device workspace of at least
+ * moe_ep_workspace_bytes() bytes, aligned to 256 bytes.  The workspace is
+ * borrowed until moe_ep_destroy and needs no initialisation.  Host-only: no
+ * device work. */
+MOE_EP_API int moe_ep_create(const moe_ep_params* params, void* workspace, size_t workspace_bytes,
+                  moe_ep_handle* out_handle);
+
+/* Sends every token to the ranks that own its selected experts
+ * (MoEEpCommunication, dispatch()) with rank-major placement
+ * (NVLinkOneSidedAlltoAll, class description): on destination d, row
+ * s*tpr + t holds token t of source s -- its hidden row, scale row, topk_ids
+ * and topk_weights, verbatim -- when d owns one of its experts and d is
+ * active.  Every other row (token not routed to d, d masked off, or
+ * t >= n_s) gets invalid_expert_id in all top_k slots and weight 0.0; its
+ * hidden and scale bytes are left unspecified.  tpr is
+ * runtime_max_tokens_per_rank, or the capacity when it is < 0.
+ * Fills results[0 .. ep_size-1] (host array) with views into the workspace.
+ * Needs the IDLE state; leaves the handle DISPATCHED.  One kernel launch. */
+MOE_EP_API int moe_ep_dispatch(moe_ep_handle handle, const moe_ep_dispatch_args* args,
+                    moe_ep_dispatch_result* results, void* stream);
+
+/* Rank `rank`'s combine input buffer: device [ep_size*tpr, hidden_size] of
+ * `dtype`, in its workspace partition, for the expert computation to write
+ * into (MoEEpCommunication and NVLinkOneSidedAlltoAll,
+ * get_combine_input_buffer()).  Valid only between dispatch and combine
+ * (ERR_STATE otherwise); dtype's size must not exceed
+ * combine_max_elem_bytes. */
+MOE_EP_API int moe_ep_get_combine_input_buffer(moe_ep_handle handle, int32_t rank, int32_t dtype,
+                                    void** out_ptr);
+
+/* For every source rank s and token t < n_s: output[s][t] = sum, over the
+ * ranks d that token was dispatched to in ascending d, of
+ * expert_output[d][s*tpr + t], accumulated in float32 from +0.0 and rounded
+ * once to dtype (bfloat16: round to nearest even).  A token that reached no
+ * rank gets zeros.  Rows of tokens not dispatched to d are never read, nor is
+ * any row of a masked-off rank (MoEEpCommunication, combine();
+ * NVLinkOneSidedAlltoAll, combine() mask rule).  Needs the DISPATCHED state;
+ * leaves the handle IDLE.  One kernel launch. */
+MOE_EP_API int moe_ep_combine(moe_ep_handle handle, const moe_ep_combine_args* args, void* stream);
+
+/* Releases the handle's host state; the workspace stays the caller's.
+ * NULL is a no-op.  Device work already enqueued with the handle must have
+ * finished before the workspace is reused (MoEEpCommunication, destroy()). */
+MOE_EP_API int moe_ep_destroy(moe_ep_handle handle);
+
+/* Bitmask with bit r set for each of the n listed ranks, all in [0, 64)
+ * (NVLinkOneSidedAlltoAll, active_rank_mask()).  ERR_MASK for a rank out of
+ * range. */
+MOE_EP_API int moe_ep_active_rank_mask(const int32_t* ranks, int32_t n, uint64_t* out_mask);
+
+/* Static text for a status code. */
+MOE_EP_API const char* moe_ep_status_string(int status);
+
+/* Description of this thread's most recent failed call ("" if none). */
+MOE_EP_API const char* moe_ep_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_EP_H */

@@ -31,9 +31,11 @@ def f32_to_bf16_bits_rne(x: np.ndarray) -> np.ndarray:
     binade and to infinity on overflow.  NaN keeps its sign and top fraction
     bits with the quiet bit set, so it stays a NaN after truncation.
     """
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    is_nan = (u & 0x7FFFFFFF) > 0x7F800000
-    lsb = (u >> 16) & 1
-    rounded = ((u + 0x7FFF + lsb) >> 16) & 0xFFFF
-    quiet_nan = ((u >> 16) | 0x0040) & 0xFFFF
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    is_nan = (u & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+    # For every non-NaN pattern (at most 0xFF800000) the sum below stays
+    # under 2^32; NaN patterns, where it may wrap, take the other branch.
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    rounded = (u + (np.uint32(0x7FFF) + lsb)) >> np.uint32(16)
+    quiet_nan = (u >> np.uint32(16)) | np.uint32(0x0040)
     return np.where(is_nan, quiet_nan, rounded).astype(np.uint16)

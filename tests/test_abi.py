@@ -1,0 +1,203 @@
+"""The C ABI on the CPU: the library loads, exports exactly what
+include/moe_ep.h declares with matching struct layouts, and its host-side
+validation returns the documented status codes before any device work.
+
+Nothing here launches a kernel: every dispatch below fails validation, and
+create only records a (fake, never dereferenced) workspace address.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from combine_token_dest_amd import _lib
+from synth import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_ep.h")
+FAKE_WS = 1 << 40            # a 256-byte aligned address that is never dereferenced
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return re.findall(r"MOE_EP_API\s+[\w\s\*]+?\b(moe_ep_\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        import combine_token_dest_amd.build as b
+        b.build()
+    return _lib.load()
+
+
+def test_exports_match_header(lib):
+    declared = header_functions()
+    assert sorted(declared) == sorted(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert exported == set(declared)
+
+
+def test_struct_layouts_match_header(lib):
+    """ctypes mirrors of the header structs have C's sizes and offsets."""
+    structs = {
+        "moe_ep_params": _lib.moe_ep_params,
+        "moe_ep_dispatch_args": _lib.moe_ep_dispatch_args,
+        "moe_ep_dispatch_result": _lib.moe_ep_dispatch_result,
+        "moe_ep_combine_args": _lib.moe_ep_combine_args,
+    }
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "moe_ep.h"', "int main(void) {"]
+    for name, cls in structs.items():
+        lines.append(f'printf("{name} sizeof %zu\\n", sizeof({name}));')
+        for f, _ in cls._fields_:
+            lines.append(f'printf("{name} {f} %zu\\n", offsetof({name}, {f}));')
+    lines.append("return 0; }")
+    with tempfile.TemporaryDirectory() as tmp:
+        src = os.path.join(tmp, "layout.c")
+        exe = os.path.join(tmp, "layout")
+        open(src, "w").write("\n".join(lines))
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), src, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout
+    for line in out.splitlines():
+        name, field, value = line.split()
+        cls = structs[name]
+        got = ctypes.sizeof(cls) if field == "sizeof" else getattr(cls, field).offset
+        assert got == int(value), f"{name}.{field}: ctypes {got} vs C {value}"
+
+
+def params(**kw):
+    base = dict(ep_size=4, num_experts=8, top_k=2, max_tokens_per_rank=16, hidden_size=128,
+                combine_max_elem_bytes=4, hidden_row_bytes=512, scale_row_bytes=0,
+                invalid_expert_id=-1, enable_rank_mask=0)
+    base.update(kw)
+    return _lib.moe_ep_params(**base)
+
+
+def status_of(fn, *args):
+    try:
+        fn(*args)
+    except _lib.MoeEpError as e:
+        return e.status
+    return _lib.MOE_EP_OK
+
+
+@pytest.mark.parametrize("w", wl.WORKLOADS, ids=[w.name for w in wl.WORKLOADS])
+def test_workspace_bytes_cover_the_regions(lib, w):
+    p = params(ep_size=w.ep_size, num_experts=w.num_experts, top_k=w.top_k,
+               max_tokens_per_rank=w.max_tokens_per_rank, hidden_size=w.hidden_size,
+               combine_max_elem_bytes=w.combine_elem_bytes, hidden_row_bytes=w.hidden_row_bytes,
+               scale_row_bytes=w.scale_row_bytes)
+    n = _lib.moe_ep_workspace_bytes(p)
+    rows = w.ep_size * w.max_tokens_per_rank
+    per_rank = rows * (w.hidden_row_bytes + w.scale_row_bytes + 8 * w.top_k
+                       + w.hidden_size * w.combine_elem_bytes)
+    assert n >= w.ep_size * per_rank + rows * 8
+    assert n <= w.ep_size * (per_rank + 6 * 4096) + rows * 8 + 4096
+    if w.name == "large":
+        assert n > 2 ** 32           # 64-bit offsets are exercised
+
+
+@pytest.mark.parametrize("bad", [
+    dict(ep_size=0), dict(ep_size=65), dict(num_experts=6, ep_size=4), dict(num_experts=2, ep_size=4),
+    dict(top_k=0), dict(max_tokens_per_rank=-1), dict(hidden_size=0), dict(combine_max_elem_bytes=3),
+    dict(hidden_row_bytes=0), dict(scale_row_bytes=-4),
+])
+def test_bad_params_rejected(lib, bad):
+    assert status_of(_lib.moe_ep_workspace_bytes, params(**bad)) == _lib.MOE_EP_ERR_INVALID_ARG
+    assert status_of(_lib.moe_ep_create, params(**bad), FAKE_WS, 1 << 30) == _lib.MOE_EP_ERR_INVALID_ARG
+
+
+def test_create_checks_workspace(lib):
+    p = params()
+    n = _lib.moe_ep_workspace_bytes(p)
+    assert status_of(_lib.moe_ep_create, p, 0, n) == _lib.MOE_EP_ERR_INVALID_ARG
+    assert status_of(_lib.moe_ep_create, p, FAKE_WS + 16, n) == _lib.MOE_EP_ERR_ALIGN
+    assert status_of(_lib.moe_ep_create, p, FAKE_WS, n - 1) == _lib.MOE_EP_ERR_INVALID_ARG
+    h = _lib.moe_ep_create(p, FAKE_WS, n)
+    assert h
+    _lib.moe_ep_destroy(h)
+    _lib.moe_ep_destroy(None)
+
+
+def dispatch_args(n, *, ids=True, hidden=True, weights=None, rtpr=-1, mask=_lib.MOE_EP_ALL_RANKS):
+    a = _lib.moe_ep_dispatch_args()
+    for s, ns in enumerate(n):
+        a.local_num_tokens[s] = ns
+        if ns:
+            a.hidden[s] = FAKE_WS + 4096 * (s + 1) if hidden else None
+            a.topk_ids[s] = FAKE_WS + 4096 * (s + 100) if ids else None
+    if weights is not None:
+        a.weights_present = weights
+        for s, ns in enumerate(n):
+            if (weights >> s) & 1 and ns:
+                a.topk_weights[s] = FAKE_WS + 4096 * (s + 200)
+    a.runtime_max_tokens_per_rank = rtpr
+    a.active_rank_mask = mask
+    return a
+
+
+def test_dispatch_validation(lib):
+    p = params()
+    h = _lib.moe_ep_create(p, FAKE_WS, _lib.moe_ep_workspace_bytes(p))
+    D = _lib.moe_ep_dispatch
+    cases = [
+        (dispatch_args([17, 0, 0, 0]), _lib.MOE_EP_ERR_CAPACITY),            # n > capacity
+        (dispatch_args([5, 0, 3, 0], rtpr=4), _lib.MOE_EP_ERR_CAPACITY),     # rtpr < largest n
+        (dispatch_args([5, 0, 3, 0], rtpr=17), _lib.MOE_EP_ERR_CAPACITY),    # rtpr > capacity
+        (dispatch_args([5, 0, 3, 0], mask=0b0011), _lib.MOE_EP_ERR_MASK),    # mask needs enable
+        (dispatch_args([5, 0, 3, 0], weights=0b0111), _lib.MOE_EP_ERR_INVALID_ARG),  # some ranks only
+        (dispatch_args([5, 0, 3, 0], hidden=False), _lib.MOE_EP_ERR_INVALID_ARG),
+        (dispatch_args([5, 0, 3, 0], ids=False), _lib.MOE_EP_ERR_INVALID_ARG),
+        (dispatch_args([-1, 0, 3, 0]), _lib.MOE_EP_ERR_INVALID_ARG),
+    ]
+    for a, want in cases:
+        assert status_of(D, h, a, 4, 0) == want, _lib.moe_ep_last_error()
+    a = dispatch_args([5, 0, 3, 0])
+    a.topk_ids[0] = FAKE_WS + 2                                               # misaligned int32
+    assert status_of(D, h, a, 4, 0) == _lib.MOE_EP_ERR_ALIGN
+    a = dispatch_args([5, 0, 3, 0])
+    a.scales_present = 0b1111                                                 # no scale rows configured
+    assert status_of(D, h, a, 4, 0) == _lib.MOE_EP_ERR_INVALID_ARG
+    # nothing was dispatched, so combine and the combine buffer are still out of order
+    ca = _lib.moe_ep_combine_args()
+    ca.active_rank_mask = _lib.MOE_EP_ALL_RANKS
+    assert status_of(_lib.moe_ep_combine, h, ca, 0) == _lib.MOE_EP_ERR_STATE
+    assert status_of(_lib.moe_ep_get_combine_input_buffer, h, 0, _lib.MOE_EP_F32) == _lib.MOE_EP_ERR_STATE
+    _lib.moe_ep_destroy(h)
+
+
+def test_mask_validation(lib):
+    p = params(enable_rank_mask=1)
+    h = _lib.moe_ep_create(p, FAKE_WS, _lib.moe_ep_workspace_bytes(p))
+    a = dispatch_args([5, 0, 3, 0], mask=0b10000)                             # bit >= ep_size
+    assert status_of(_lib.moe_ep_dispatch, h, a, 4, 0) == _lib.MOE_EP_ERR_MASK
+    _lib.moe_ep_destroy(h)
+
+
+def test_active_rank_mask(lib):
+    assert _lib.moe_ep_active_rank_mask([0, 2, 5]) == 0b100101
+    assert _lib.moe_ep_active_rank_mask([]) == 0
+    assert _lib.moe_ep_active_rank_mask([63, 0]) == (1 << 63) | 1
+    assert status_of(_lib.moe_ep_active_rank_mask, [64]) == _lib.MOE_EP_ERR_MASK
+    assert status_of(_lib.moe_ep_active_rank_mask, [-1]) == _lib.MOE_EP_ERR_MASK
+
+
+def test_status_strings(lib):
+    for code, name in [(0, "MOE_EP_OK"), (-1, "MOE_EP_ERR_INVALID_ARG"), (-2, "MOE_EP_ERR_STATE"),
+                       (-3, "MOE_EP_ERR_CAPACITY"), (-4, "MOE_EP_ERR_MASK"), (-5, "MOE_EP_ERR_ALIGN"),
+                       (-6, "MOE_EP_ERR_HIP"), (-7, "MOE_EP_ERR_UNSUPPORTED")]:
+        assert _lib.moe_ep_status_string(code) == name
+
+
+def test_platform_query_does_not_crash(lib):
+    assert _lib.moe_ep_is_platform_supported() in (True, False)

@@ -1,0 +1,337 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every test prints the case it runs before touching the GPU.
+"""
+
+from __future__ import annotations
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import workloads as wl
+from tests import parity
+from tests.golden_cases import all_cases
+from tests.parity import Case, log
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = all_cases()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from combine_token_dest_amd import _lib
+    _lib.load()      # raises when the library is missing: no fallback
+    assert _lib.moe_ep_is_platform_supported(), "not a gfx950 device"
+
+
+# --------------------------------------------------------------------------
+# The five workloads at full size
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name", [w.name for w in wl.WORKLOADS])
+def test_workload_full_size(name):
+    w = wl.BY_NAME[name]
+    log(f"[parity] workload {name} seed {w.seed}")
+    c = parity.case_from_workload(w)
+    parity.run_step(c, zero_copy=True)
+
+
+@pytest.mark.parametrize("name", ["dsv3", "ragged"])
+def test_workload_separate_combine_input(name):
+    w = wl.BY_NAME[name]
+    log(f"[parity] workload {name} separate expert_output tensors")
+    c = parity.case_from_workload(w)
+    parity.run_step(c, zero_copy=False)
+
+
+def test_ragged_steps_on_one_handle():
+    """Steps with different local counts and tokens_per_rank reuse one handle."""
+    w = wl.BY_NAME["ragged"]
+    c0 = parity.case_from_workload(w)
+    moe = parity.make_gpu(c0)
+    for i, nt in enumerate([[5, 0, 300, 512, 0, 1, 17, 64], [0] * 8, [1, 0, 0, 0, 0, 0, 0, 0],
+                            [512] * 8, [3, 0, 2, 9, 0, 0, 4, 1]]):
+        log(f"[parity] ragged step {i} n={nt}")
+        c = parity.case_from_workload(w, local_num_tokens=nt, seed=2000 + i)
+        parity.run_step(c, moe=moe)
+    moe.destroy()
+
+
+# --------------------------------------------------------------------------
+# Hand-worked examples through the GPU
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("case", GOLDEN, ids=[g.name for g in GOLDEN])
+def test_golden_on_gpu(case):
+    log(f"[parity] golden {case.name}")
+    p = case.params
+    c = Case(p["ep_size"], p["num_experts"], p["top_k"], p["max_tokens_per_rank"], p["hidden_size"],
+             p["hidden_row_bytes"], p["scale_row_bytes"], case.hidden, case.topk_ids, case.topk_weights,
+             case.scale, None, case.runtime_max_tokens_per_rank, case.active_rank_mask, case.combine_dtype,
+             invalid_id=p["invalid_expert_id"], enable_rank_mask=bool(p["enable_rank_mask"]), name=case.name)
+    moe = parity.make_gpu(c)
+    hid, ids, w, sc = parity.upload(c)
+    res = moe.dispatch(hid, ids, w, hidden_states_scale=sc, runtime_max_tokens_per_rank=c.rtpr,
+                       active_rank_mask=c.mask)
+    e = case.expect
+    for d in range(c.ep):
+        assert res[d].tokens_per_rank == e["tokens_per_rank"]
+        np.testing.assert_array_equal(res[d].topk_ids.cpu().numpy(), np.array(e["topk_ids"][d], np.int32))
+        np.testing.assert_array_equal(res[d].topk_weights.cpu().numpy(),
+                                      np.array(e["topk_weights"][d], np.float32))
+        gh = res[d].hidden.view(torch.uint8).cpu().numpy().reshape(-1, c.H)
+        for r, row in e["hidden_valid_rows"][d].items():
+            np.testing.assert_array_equal(gh[int(r)], np.array(row, np.uint8))
+        if "scale_valid_rows" in e:
+            gs = res[d].hidden_scale.view(torch.uint8).cpu().numpy().reshape(-1, c.S)
+            for r, row in e["scale_valid_rows"][d].items():
+                np.testing.assert_array_equal(gs[int(r)], np.array(row, np.uint8))
+    eo = [parity.host_to_torch(case.expert_output[d], c.combine_dtype) for d in range(c.ep)]
+    out = moe.combine(eo, active_rank_mask=case.combine_mask)
+    for s in range(c.ep):
+        g = parity.torch_to_host(out[s], c.combine_dtype)
+        if c.combine_dtype == "f32":
+            np.testing.assert_array_equal(g, case.expect_combine[s])
+        else:
+            np.testing.assert_array_equal(g, case.expect_combine[s])
+    moe.destroy()
+
+
+# --------------------------------------------------------------------------
+# Edge cases: shapes, vector widths, masks, ids, empty ranks
+# --------------------------------------------------------------------------
+def random_case(seed, ep, E, K, cap, n, hidden_size, H, S=0, rtpr=None, mask=None, dtype="bf16",
+                weights=True, invalid=-1, id_lo=None, id_hi=None, name=""):
+    rng = np.random.default_rng(seed)
+    lo = 0 if id_lo is None else id_lo
+    hi = E if id_hi is None else id_hi
+    ids = [rng.integers(lo, hi, size=(n[s], K)).astype(np.int32) for s in range(ep)]
+    hidden = [rng.integers(0, 256, size=(n[s], H)).astype(np.uint8) for s in range(ep)]
+    w = [rng.standard_normal((n[s], K)).astype(np.float32) for s in range(ep)] if weights else None
+    sc = [rng.integers(0, 256, size=(n[s], S)).astype(np.uint8) for s in range(ep)] if S else None
+    return Case(ep, E, K, cap, hidden_size, H, S, hidden, ids, w, sc, None, rtpr, mask, dtype,
+                invalid_id=invalid, enable_rank_mask=mask is not None, name=name)
+
+
+EDGE = [
+    # name, kwargs
+    ("ep1", dict(ep=1, E=4, K=2, cap=7, n=[7], hidden_size=64, H=128)),
+    ("ep3_oddK", dict(ep=3, E=9, K=3, cap=33, n=[33, 0, 20], hidden_size=100, H=200)),
+    ("ep5_rtpr", dict(ep=5, E=10, K=4, cap=64, n=[3, 40, 0, 17, 1], hidden_size=130, H=260, rtpr=50)),
+    ("vec8_hidden", dict(ep=4, E=8, K=2, cap=9, n=[9, 9, 9, 9], hidden_size=4, H=24)),
+    ("vec4_hidden", dict(ep=4, E=8, K=2, cap=9, n=[9, 2, 9, 0], hidden_size=6, H=12)),
+    ("vec2_hidden", dict(ep=4, E=8, K=2, cap=9, n=[1, 2, 3, 4], hidden_size=3, H=6)),
+    ("vec1_hidden", dict(ep=4, E=8, K=2, cap=9, n=[9, 8, 7, 6], hidden_size=7, H=7)),
+    ("f32_odd_hidden", dict(ep=4, E=8, K=2, cap=12, n=[12, 5, 0, 11], hidden_size=37, H=148, dtype="f32")),
+    ("f32_hidden2", dict(ep=2, E=2, K=1, cap=5, n=[5, 4], hidden_size=2, H=8, dtype="f32")),
+    ("bf16_hidden1", dict(ep=3, E=3, K=2, cap=5, n=[5, 4, 3], hidden_size=1, H=2)),
+    ("scales_odd", dict(ep=4, E=16, K=4, cap=16, n=[16, 3, 0, 9], hidden_size=256, H=256, S=13)),
+    ("scales_vec4", dict(ep=4, E=16, K=4, cap=16, n=[16, 3, 0, 9], hidden_size=256, H=256, S=36)),
+    ("ids_out_of_range", dict(ep=4, E=8, K=4, cap=10, n=[10, 10, 10, 10], hidden_size=64, H=128,
+                              id_lo=-3, id_hi=12)),
+    ("invalid_is_E", dict(ep=4, E=8, K=2, cap=10, n=[10, 0, 10, 3], hidden_size=64, H=128, invalid=8)),
+    ("mask_some", dict(ep=8, E=64, K=6, cap=40, n=[40, 39, 0, 1, 2, 40, 13, 7], hidden_size=512, H=1024,
+                       mask=0b10110101)),
+    ("mask_none_active", dict(ep=4, E=8, K=2, cap=8, n=[8, 8, 8, 8], hidden_size=32, H=64, mask=0)),
+    ("no_weights", dict(ep=4, E=8, K=3, cap=8, n=[8, 1, 0, 5], hidden_size=32, H=64, weights=False)),
+    ("big_row_multi_pass", dict(ep=2, E=4, K=2, cap=6, n=[6, 5], hidden_size=40000, H=80000)),
+    ("k16", dict(ep=8, E=256, K=16, cap=32, n=[32] * 8, hidden_size=128, H=256)),
+    ("wide_ep64", dict(ep=64, E=128, K=8, cap=4, n=[4] * 64, hidden_size=64, H=128,
+                       mask=((1 << 64) - 1) & ~(1 << 5))),
+    ("ep64_bit63_only", dict(ep=64, E=64, K=4, cap=3, n=[3] * 64, hidden_size=16, H=32, mask=1 << 63)),
+    ("all_empty_cap", dict(ep=4, E=8, K=2, cap=6, n=[0, 0, 0, 0], hidden_size=16, H=32)),
+    ("all_empty_rtpr0", dict(ep=4, E=8, K=2, cap=6, n=[0, 0, 0, 0], hidden_size=16, H=32, rtpr=0)),
+    ("cap0", dict(ep=2, E=2, K=1, cap=0, n=[0, 0], hidden_size=16, H=32)),
+]
+
+
+@pytest.mark.parametrize("name,kw", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_case(name, kw):
+    log(f"[parity] edge {name}")
+    c = random_case(zlib.crc32(name.encode()) % 10000, name=name, **kw)
+    parity.run_step(c, zero_copy=True)
+    parity.run_step(c, zero_copy=False)
+
+
+def test_misaligned_rows_use_narrow_vectors():
+    """Row pointers offset by 1, 2, 4 and 8 bytes from 16-byte alignment."""
+    for off in (1, 2, 4, 8):
+        log(f"[parity] misaligned hidden pointers offset {off}")
+        c = random_case(off, ep=3, E=6, K=2, cap=8, n=[8, 3, 5], hidden_size=256, H=512, name=f"mis{off}")
+        p = parity.oracle_params(c)
+        om = oracle.OracleMoEEp(p)
+        ores = om.dispatch(c.hidden, c.ids, c.weights)
+        moe = parity.make_gpu(c)
+        hid = []
+        for h in c.hidden:
+            big = torch.zeros(h.size + 64, dtype=torch.uint8, device="cuda")
+            view = big[off:off + h.size].view(h.shape)
+            view.copy_(torch.from_numpy(h).cuda())
+            hid.append(view)
+        ids = [parity.to_dev(i) for i in c.ids]
+        w = [parity.to_dev(x) for x in c.weights]
+        gres = moe.dispatch(hid, ids, w)
+        parity.compare_dispatch(c, gres, ores, f"mis{off}")
+        eo_host = parity.combine_inputs_host(c, ores)
+        oout = om.combine(eo_host, "bf16")
+        # misaligned expert_output and output by one element (2 bytes)
+        eo = []
+        for d in range(c.ep):
+            big = torch.zeros(eo_host[d].size + 16, dtype=torch.bfloat16, device="cuda")
+            v = big[1:1 + eo_host[d].size].view(eo_host[d].shape)
+            v.copy_(parity.host_to_torch(eo_host[d], "bf16"))
+            eo.append(v)
+        outs = []
+        for s in range(c.ep):
+            big = torch.zeros(c.n[s] * c.hidden_size + 16, dtype=torch.bfloat16, device="cuda")
+            outs.append(big[3:3 + c.n[s] * c.hidden_size].view(c.n[s], c.hidden_size))
+        gout = moe.combine(eo, output=outs)
+        torch.cuda.synchronize()
+        parity.compare_combine(c, gout, oout, f"mis{off}")
+        moe.destroy()
+
+
+def test_expert_output_3d_form():
+    """[ep, tpr, hidden] is accepted as the same memory as [ep*tpr, hidden]."""
+    log("[parity] expert_output as [ep, tpr, hidden]")
+    c = random_case(5, ep=4, E=8, K=2, cap=10, n=[10, 4, 0, 7], hidden_size=96, H=192)
+    p = parity.oracle_params(c)
+    om = oracle.OracleMoEEp(p)
+    ores = om.dispatch(c.hidden, c.ids, c.weights)
+    eo_host = parity.combine_inputs_host(c, ores)
+    oout = om.combine(eo_host, "bf16")
+    moe = parity.make_gpu(c)
+    hid, ids, w, _ = parity.upload(c)
+    moe.dispatch(hid, ids, w)
+    tpr = 10
+    eo = [parity.host_to_torch(eo_host[d], "bf16").view(c.ep, tpr, c.hidden_size) for d in range(c.ep)]
+    gout = moe.combine(eo)
+    torch.cuda.synchronize()
+    parity.compare_combine(c, gout, oout, "3d")
+    moe.destroy()
+
+
+# --------------------------------------------------------------------------
+# Writes stay where the method puts them; reads skip what it never needs
+# --------------------------------------------------------------------------
+def test_writes_stay_in_bounds():
+    """Workspace bytes the step has no business touching keep a canary, and
+    output guard bands stay intact."""
+    log("[parity] canary / guard bands")
+    c = random_case(11, ep=4, E=8, K=2, cap=16, n=[9, 0, 12, 5], hidden_size=64, H=128, S=20, rtpr=12)
+    p = parity.oracle_params(c)
+    om = oracle.OracleMoEEp(p)
+    ores = om.dispatch(c.hidden, c.ids, c.weights, hidden_states_scale=c.scale, runtime_max_tokens_per_rank=12)
+    moe = parity.make_gpu(c)
+    moe.workspace.fill_(0x5A)
+    hid, ids, w, sc = parity.upload(c)
+    gres = moe.dispatch(hid, ids, w, hidden_states_scale=sc, runtime_max_tokens_per_rank=12)
+    torch.cuda.synchronize()
+    parity.compare_dispatch(c, gres, ores, "canary")
+    tpr = 12
+    rows = c.ep * tpr
+    for d in range(c.ep):
+        # hidden / scale bytes of invalid rows are not written
+        gh = gres[d].hidden.view(torch.uint8).cpu().numpy().reshape(rows, c.H)
+        assert (gh[~ores[d].valid] == 0x5A).all()
+        gs = gres[d].hidden_scale.view(torch.uint8).cpu().numpy().reshape(rows, c.S)
+        assert (gs[~ores[d].valid] == 0x5A).all()
+        # rows past ep*tpr of the capacity-sized regions are not written
+        ws = moe.workspace
+        base = gres[d].hidden.data_ptr() - ws.data_ptr()
+        tail = ws[base + rows * c.H: base + c.ep * c.cap * c.H].cpu().numpy()
+        assert (tail == 0x5A).all()
+        ib = gres[d].topk_ids.data_ptr() - ws.data_ptr()
+        tail = ws[ib + rows * c.K * 4: ib + c.ep * c.cap * c.K * 4].cpu().numpy()
+        assert (tail == 0x5A).all()
+        # dispatch leaves the combine input buffer alone
+        cb = moe.get_combine_input_buffer(d, torch.bfloat16)
+        assert (cb.view(torch.uint8).cpu().numpy() == 0x5A).all()
+    eo_host = parity.combine_inputs_host(c, ores)
+    oout = om.combine(eo_host, "bf16")
+    eo = [parity.host_to_torch(eo_host[d], "bf16") for d in range(c.ep)]
+    guard = 64
+    outs, bigs = [], []
+    for s in range(c.ep):
+        big = torch.full((c.n[s] * c.hidden_size + 2 * guard,), 7.0, dtype=torch.bfloat16, device="cuda")
+        bigs.append(big)
+        outs.append(big[guard:guard + c.n[s] * c.hidden_size].view(c.n[s], c.hidden_size))
+    gout = moe.combine(eo, output=outs)
+    torch.cuda.synchronize()
+    parity.compare_combine(c, gout, oout, "canary")
+    for s in range(c.ep):
+        b = bigs[s].float().cpu().numpy()
+        assert (b[:guard] == 7.0).all() and (b[len(b) - guard:] == 7.0).all()
+    moe.destroy()
+
+
+def test_masked_rank_buffers_never_read():
+    """NaN in every row of a masked-off rank and in every unrouted row."""
+    log("[parity] NaN poison on masked ranks")
+    w = wl.BY_NAME["ragged"]
+    c = parity.case_from_workload(w, local_num_tokens=[50, 0, 31, 7, 0, 0, 64, 9])
+    p = parity.oracle_params(c)
+    om = oracle.OracleMoEEp(p)
+    ores = om.dispatch(c.hidden, c.ids, c.weights, runtime_max_tokens_per_rank=c.rtpr, active_rank_mask=c.mask)
+    eo_host = [a.copy() for a in parity.combine_inputs_host(c, ores)]
+    for d in w.masked_ranks:
+        eo_host[d][:] = 0x7FC0
+    oout = om.combine(eo_host, "bf16", active_rank_mask=c.mask)
+    moe = parity.make_gpu(c)
+    hid, ids, wt, _ = parity.upload(c)
+    moe.dispatch(hid, ids, wt, runtime_max_tokens_per_rank=c.rtpr, active_rank_mask=c.mask)
+    eo = [parity.host_to_torch(eo_host[d], "bf16") for d in range(c.ep)]
+    gout = moe.combine(eo, active_rank_mask=c.mask)
+    torch.cuda.synchronize()
+    parity.compare_combine(c, gout, oout, "poison")
+    moe.destroy()
+
+
+# --------------------------------------------------------------------------
+# Call protocol on the GPU path
+# --------------------------------------------------------------------------
+def test_call_protocol_errors_leave_state_unchanged():
+    from combine_token_dest_amd import MoeEpError, _lib
+    log("[parity] call protocol")
+    c = random_case(3, ep=4, E=8, K=2, cap=8, n=[8, 2, 0, 5], hidden_size=32, H=64, mask=0b1011)
+    moe = parity.make_gpu(c)
+    hid, ids, w, _ = parity.upload(c)
+    with pytest.raises(MoeEpError) as e:
+        moe.combine([None] * c.ep, active_rank_mask=0b1011)
+    assert e.value.status == _lib.MOE_EP_ERR_STATE
+    with pytest.raises(MoeEpError) as e:
+        moe.get_combine_input_buffer(0, torch.bfloat16)
+    assert e.value.status == _lib.MOE_EP_ERR_STATE
+    moe.dispatch(hid, ids, w, active_rank_mask=0b1011)
+    with pytest.raises(MoeEpError) as e:
+        moe.dispatch(hid, ids, w, active_rank_mask=0b1011)
+    assert e.value.status == _lib.MOE_EP_ERR_STATE
+    with pytest.raises(MoeEpError) as e:
+        moe.combine([None] * c.ep, active_rank_mask=0b1111)
+    assert e.value.status == _lib.MOE_EP_ERR_MASK
+    with pytest.raises(MoeEpError) as e:
+        moe.combine([None] * c.ep)
+    assert e.value.status == _lib.MOE_EP_ERR_MASK
+    outs = moe.combine([moe.get_combine_input_buffer(d, torch.bfloat16) for d in range(c.ep)],
+                       active_rank_mask=0b1011)
+    torch.cuda.synchronize()
+    assert [tuple(o.shape) for o in outs] == [(8, 32), (2, 32), (0, 32), (5, 32)]
+    moe.destroy()
+    moe.destroy()
+
+
+def test_two_instances_interleaved():
+    log("[parity] two instances")
+    c1 = parity.case_from_workload(wl.BY_NAME["tiny"])
+    c2 = random_case(8, ep=3, E=6, K=2, cap=5, n=[5, 1, 4], hidden_size=48, H=96, name="second")
+    m1, m2 = parity.make_gpu(c1), parity.make_gpu(c2)
+    parity.run_step(c1, moe=m1)
+    parity.run_step(c2, moe=m2)
+    parity.run_step(c1, moe=m1)
+    m1.destroy()
+    m2.destroy()

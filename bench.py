@@ -205,6 +205,47 @@ def cpu_baseline(w, inp, bytes_per_round, seconds):
             "host_cpus": os.cpu_count(), "host_affinity": len(os.sched_getaffinity(0))}
 
 
+class HipEvents:
+    """HIP events created with hipEventDisableSystemFence: recording one adds
+    no system-scope release (no L2 writeback between the kernels it
+    brackets), so launch-to-launch event pairs time the kernels themselves."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")      # the runtime torch already loaded
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        st = self.hip.hipEventCreateWithFlags(ctypes.byref(ev), self.DISABLE_SYSTEM_FENCE)
+        if st:
+            raise RuntimeError(f"hipEventCreateWithFlags: {st}")
+        return ev
+
+    def record(self, ev, stream):
+        st = self.hip.hipEventRecord(ev, ctypes.c_void_p(stream))
+        if st:
+            raise RuntimeError(f"hipEventRecord: {st}")
+
+    def elapsed_ms(self, a, b):
+        st = self.hip.hipEventSynchronize(b)
+        if st:
+            raise RuntimeError(f"hipEventSynchronize: {st}")
+        ms = ctypes.c_float()
+        st = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if st:
+            raise RuntimeError(f"hipEventElapsedTime: {st}")
+        return ms.value
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ev)
+
+
 def kernel_source_hash():
     with open(KERNEL_SOURCE, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -294,23 +335,27 @@ def main():
 
     # Timed region: K steps, HIP events around every launch on the launch stream.
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    hev = HipEvents()
+    ev = [[hev.create() for _ in range(3)] for _ in range(K)]
     log(f"[bench] timing {K} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         inst = insts[i % I]
         e = ev[i]
-        e[0].record(stream)
+        hev.record(e[0], sp)
         inst.dispatch(sp)
-        e[1].record(stream)
+        hev.record(e[1], sp)
         inst.combine(sp)
-        e[2].record(stream)
+        hev.record(e[2], sp)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall_s = t1 - t0
-    d_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)])
-    c_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)])
+    d_ms = np.array([hev.elapsed_ms(ev[i][0], ev[i][1]) for i in range(K)])
+    c_ms = np.array([hev.elapsed_ms(ev[i][1], ev[i][2]) for i in range(K)])
+    for e in ev:
+        for x in e:
+            hev.destroy(x)
 
     # Same steps without events, for the event overhead on the step time.
     torch.cuda.synchronize()

@@ -69,8 +69,9 @@ struct CombineKArgs {
 };
 
 struct LaunchShape {
-  int grid;
-  int block;
+  int grid_x;   // rows (dispatch) or real tokens (combine)
+  int grid_y;   // column chunks of a row
+  int block;    // threads per workgroup
 };
 
 // Enqueue one dispatch kernel.  vec_bytes in {16, 8, 4, 2, 1} must divide

@@ -9,6 +9,8 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <climits>
+#include <cstdint>
 #include <cstring>
 #include <new>
 #include <string>
@@ -91,7 +93,8 @@ int validate_params(const moe_ep_params* p) {
   // Row and grid indices are 32-bit in the kernels; byte offsets are 64-bit.
   const int64_t rows = (int64_t)p->ep_size * p->max_tokens_per_rank;
   if (rows > (int64_t)1 << 30) return fail(MOE_EP_ERR_INVALID_ARG, "ep_size * capacity too large");
-  if (p->hidden_row_bytes > ((int64_t)1 << 31) || p->scale_row_bytes > ((int64_t)1 << 31))
+  // Rows are addressed with 32-bit byte offsets inside the kernels.
+  if (p->hidden_row_bytes > INT32_MAX || p->scale_row_bytes > INT32_MAX || p->hidden_size > INT32_MAX / 4)
     return fail(MOE_EP_ERR_INVALID_ARG, "row bytes too large");
   return ok();
 }

@@ -51,29 +51,53 @@ __device__ __forceinline__ int expert_owner(const OwnerDiv& od, uint32_t e) {
   return (int)(((uint64_t)e * od.magic) >> od.shift);
 }
 
-// Loads and stores through the global address space (pointers read from
-// the kernel-argument tables would otherwise be treated as flat).  NT marks
-// them nontemporal: the data is streamed once and should not displace
-// anything in the caches.
-#define MOE_EP_GLOBAL __attribute__((address_space(1)))
+// Row accesses go through buffer resources: one resource per row (base
+// address, byte size) lets the hardware discard any access past the row,
+// lanes need only 32-bit offsets, and the instruction carries an explicit
+// cache policy (CP):
+//   0 = default, 2 = nt (nontemporal), 16 = sc1, 17 = sc0 sc1, 18 = sc1 nt.
+enum : int { kCpDefault = 0, kCpNt = 2, kCpSc1 = 16, kCpSc0Sc1 = 17, kCpSc1Nt = 18 };
 
-template <bool NT, typename V>
-__device__ __forceinline__ void store(V* p, const V& v) {
-  MOE_EP_GLOBAL V* g = (MOE_EP_GLOBAL V*)p;
-  if constexpr (NT) {
-    __builtin_nontemporal_store(v, g);
+// Buffer resource word 3 for raw (unswizzled, stride 0) buffers on gfx9-class parts.
+constexpr int kRawBufferFlags = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRawBufferFlags);
+}
+
+template <int VB, int CP>
+__device__ __forceinline__ typename Bytes<VB>::type buf_load(__amdgpu_buffer_rsrc_t r, int off) {
+  typedef typename Bytes<VB>::type V;
+  if constexpr (VB == 16) {
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CP));
+  } else if constexpr (VB == 8) {
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, CP));
+  } else if constexpr (VB == 4) {
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CP));
+  } else if constexpr (VB == 2) {
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, CP));
   } else {
-    *g = v;
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, CP));
   }
 }
 
-template <bool NT, typename V>
-__device__ __forceinline__ V load(const V* p) {
-  const MOE_EP_GLOBAL V* g = (const MOE_EP_GLOBAL V*)p;
-  if constexpr (NT) {
-    return __builtin_nontemporal_load(g);
+template <int VB, int CP>
+__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, int off, const typename Bytes<VB>::type& v) {
+  if constexpr (VB == 16) {
+    typedef decltype(__builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 0)) W;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(W, v), r, off, 0, CP);
+  } else if constexpr (VB == 8) {
+    typedef decltype(__builtin_amdgcn_raw_buffer_load_b64(r, 0, 0, 0)) W;
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(W, v), r, off, 0, CP);
+  } else if constexpr (VB == 4) {
+    typedef decltype(__builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, 0)) W;
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(W, v), r, off, 0, CP);
+  } else if constexpr (VB == 2) {
+    typedef decltype(__builtin_amdgcn_raw_buffer_load_b16(r, 0, 0, 0)) W;
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(W, v), r, off, 0, CP);
   } else {
-    return *g;
+    typedef decltype(__builtin_amdgcn_raw_buffer_load_b8(r, 0, 0, 0)) W;
+    __builtin_amdgcn_raw_buffer_store_b8(__builtin_bit_cast(W, v), r, off, 0, CP);
   }
 }
 
@@ -85,7 +109,7 @@ __device__ __forceinline__ V load(const V* p) {
 // writes the route mask, the ids/weights slot of row r on every rank and the
 // scale row.  Each thread holds U vectors of VB bytes of its column chunk.
 // ---------------------------------------------------------------------------
-template <int VB, int U, bool NT>
+template <int VB, int U, int LP, int SP>
 __device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const int r) {
   typedef typename Bytes<VB>::type V;
   const int s = r / a.tpr;
@@ -95,13 +119,13 @@ __device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const int r
   const int32_t* __restrict__ idr = a.ids[s] + (int64_t)t * K;
   const int64_t nv = a.hidden_bytes / VB;
   const int64_t per_block = (int64_t)blockDim.x * U;
-  const V* __restrict__ src = reinterpret_cast<const V*>(a.hidden[s] + (int64_t)t * a.hidden_bytes);
+  const __amdgpu_buffer_rsrc_t src = row_rsrc(a.hidden[s] + (int64_t)t * a.hidden_bytes, a.hidden_bytes);
   const int64_t c_first = (int64_t)blockIdx.y * per_block;
 
   // The first chunk of the token's hidden row is loaded before the routing
   // is known, so its latency overlaps that of the expert ids.  Lanes past
   // the end of the row load column 0 (in bounds) and store nothing.
-  int64_t col[U];
+  int off[U];
   bool live[U];
   V v[U];
   if (real && c_first < nv) {
@@ -109,8 +133,8 @@ __device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const int r
     for (int u = 0; u < U; ++u) {
       const int64_t c = c_first + threadIdx.x + (int64_t)u * blockDim.x;
       live[u] = c < nv;
-      col[u] = live[u] ? c : 0;
-      v[u] = load<NT>(src + col[u]);
+      off[u] = live[u] ? (int)(c * VB) : 0;
+      v[u] = buf_load<VB, LP>(src, off[u]);
     }
   }
 
@@ -192,18 +216,18 @@ __device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const int r
       for (int u = 0; u < U; ++u) {
         const int64_t c = c0 + threadIdx.x + (int64_t)u * blockDim.x;
         live[u] = c < nv;
-        col[u] = live[u] ? c : 0;
-        v[u] = load<NT>(src + col[u]);
+        off[u] = live[u] ? (int)(c * VB) : 0;
+        v[u] = buf_load<VB, LP>(src, off[u]);
       }
     }
     uint64_t mm = m;
     while (mm) {
       const int d = __builtin_ctzll(mm);
       mm &= mm - 1;
-      V* __restrict__ dst = reinterpret_cast<V*>(a.ws + (int64_t)d * a.part_stride + dst_off);
+      const __amdgpu_buffer_rsrc_t dst = row_rsrc(a.ws + (int64_t)d * a.part_stride + dst_off, a.hidden_bytes);
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (live[u]) store<NT>(dst + col[u], v[u]);
+        if (live[u]) buf_store<VB, SP>(dst, off[u], v[u]);
     }
   }
 }
@@ -211,11 +235,11 @@ __device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const int r
 // Grid: x strides over the receive rows r = s*tpr + t (one row per
 // workgroup when the grid is as large as the row count), y = column chunk
 // of the hidden row.
-template <int VB, int U, bool NT>
+template <int VB, int U, int LP, int SP>
 __global__ void __launch_bounds__(kMaxBlock)
 dispatch_kernel(const DispatchKArgs a) {
   const int rows = a.ep * a.tpr;
-  for (int r = blockIdx.x; r < rows; r += gridDim.x) dispatch_row<VB, U, NT>(a, r);
+  for (int r = blockIdx.x; r < rows; r += gridDim.x) dispatch_row<VB, U, LP, SP>(a, r);
 }
 
 // ---------------------------------------------------------------------------
@@ -274,7 +298,7 @@ __device__ __forceinline__ typename CVec<DT, VE>::type pack(const float (&acc)[V
   return v;
 }
 
-template <int DT, int VE, int U, int DB, bool NT>
+template <int DT, int VE, int U, int DB, int LP, int SP>
 __device__ __forceinline__ void combine_token(const CombineKArgs& a, const int b) {
   typedef typename CVec<DT, VE>::type V;
   int s = 0;
@@ -286,19 +310,20 @@ __device__ __forceinline__ void combine_token(const CombineKArgs& a, const int b
   constexpr int esz = DT == MOE_EP_F32 ? 4 : 2;
   const int64_t row_bytes = a.hidden * esz;
   const int64_t per_block = (int64_t)blockDim.x * U;
-  V* __restrict__ out = reinterpret_cast<V*>(a.output[s] + (int64_t)t * row_bytes);
+  constexpr int VB = VE * esz;
+  const __amdgpu_buffer_rsrc_t out = row_rsrc(a.output[s] + (int64_t)t * row_bytes, row_bytes);
 
   for (int64_t c0 = (int64_t)blockIdx.y * per_block; c0 < nv; c0 += (int64_t)gridDim.y * per_block) {
     // Lanes past the end of the row read column 0 (in bounds) and store
     // nothing, so every load below is unconditional and they all issue
     // before the first add waits.
-    int64_t col[U];
+    int off[U];
     bool live[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t c = c0 + threadIdx.x + (int64_t)u * blockDim.x;
       live[u] = c < nv;
-      col[u] = live[u] ? c : 0;
+      off[u] = live[u] ? (int)(c * VB) : 0;
     }
     float acc[U][VE];
 #pragma unroll
@@ -310,14 +335,14 @@ __device__ __forceinline__ void combine_token(const CombineKArgs& a, const int b
     while (mm) {
       // The next DB destination rows in ascending rank order; slots past the
       // last one repeat it (its loads are already in flight) and add +0.0.
-      const V* rows[DB];
+      __amdgpu_buffer_rsrc_t rows[DB];
       int cnt = 0;
 #pragma unroll
       for (int k = 0; k < DB; ++k) {
         if (mm) {
           const int d = __builtin_ctzll(mm);
           mm &= mm - 1;
-          rows[k] = reinterpret_cast<const V*>(a.expert_output[d] + r * row_bytes);
+          rows[k] = row_rsrc(a.expert_output[d] + r * row_bytes, row_bytes);
           cnt = k + 1;
         } else {
           rows[k] = rows[k > 0 ? k - 1 : 0];
@@ -327,7 +352,7 @@ __device__ __forceinline__ void combine_token(const CombineKArgs& a, const int b
 #pragma unroll
       for (int k = 0; k < DB; ++k)
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[k][u] = load<NT>(rows[k] + col[u]);
+        for (int u = 0; u < U; ++u) v[k][u] = buf_load<VB, LP>(rows[k], off[u]);
 #pragma unroll
       for (int k = 0; k < DB; ++k)
 #pragma unroll
@@ -335,17 +360,17 @@ __device__ __forceinline__ void combine_token(const CombineKArgs& a, const int b
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (live[u]) store<NT>(out + col[u], pack<DT, VE>(acc[u]));
+      if (live[u]) buf_store<VB, SP>(out, off[u], pack<DT, VE>(acc[u]));
   }
 }
 
 // Grid: x strides over the real tokens (prefix over source ranks), y =
 // column chunk of the row.
-template <int DT, int VE, int U, int DB, bool NT>
+template <int DT, int VE, int U, int DB, int LP, int SP>
 __global__ void __launch_bounds__(kMaxBlock)
 combine_kernel(const CombineKArgs a) {
   const int tokens = a.token_start[a.ep];
-  for (int b = blockIdx.x; b < tokens; b += gridDim.x) combine_token<DT, VE, U, DB, NT>(a, b);
+  for (int b = blockIdx.x; b < tokens; b += gridDim.x) combine_token<DT, VE, U, DB, LP, SP>(a, b);
 }
 
 int round_block(int64_t threads) {
@@ -359,22 +384,25 @@ int round_block(int64_t threads) {
 
 // Launch configurations, chosen by timing variants on MI355X with the
 // DeepSeek-V3-shaped round (ep 8, 128 tokens per rank, 14 KiB rows) and the
-// 32-rank, 8 KiB-row round:
+// 32-rank, 8 KiB-row round, rotating over enough workspaces that the 256 MB
+// MALL holds none of the data between uses:
 //  - dispatch: 8 vectors of 16 B per thread and up to 128 threads, so one
-//    workgroup carries up to 16 KiB of a row; nontemporal loads and stores
-//    (the rows are streamed once) were 4-8% faster than cached ones.
+//    workgroup carries up to 16 KiB of a row.
 //  - combine: 2 column vectors per thread, destination rows loaded 4 at a
-//    time, up to 512 threads (a whole 14 KiB bf16 row per workgroup);
-//    nontemporal accesses were ~10% faster.
+//    time, up to 512 threads (a whole 14 KiB bf16 row per workgroup).
+//  - nontemporal loads and stores in both: cached combine loads were ~40%
+//    slower, and sc1 (or sc0 sc1) dispatch stores ~8% slower.
 //  Capping the grid below one workgroup per row (persistent loops) was
 //  slower for both kernels.
 constexpr int kDispatchU = 8;
 constexpr int kDispatchBlock = 128;
-constexpr bool kDispatchNT = true;
+constexpr int kDispatchLP = kCpNt;
+constexpr int kDispatchSP = kCpNt;
 constexpr int kCombineU = 2;
 constexpr int kCombineDB = 4;
 constexpr int kCombineBlock = 512;
-constexpr bool kCombineNT = true;
+constexpr int kCombineLP = kCpNt;
+constexpr int kCombineSP = kCpNt;
 
 LaunchShape dispatch_shape(int64_t rows, int64_t hidden_bytes, int vec_bytes) {
   const int64_t nv = hidden_bytes / vec_bytes;
@@ -398,7 +426,7 @@ hipError_t launch_dispatch(const DispatchKArgs& a, int vec_bytes, hipStream_t st
   const void* fn;
   switch (vec_bytes) {
 #define MOE_EP_D(VB) \
-    case VB: fn = reinterpret_cast<const void*>(&dispatch_kernel<VB, kDispatchU, kDispatchNT>); break;
+    case VB: fn = reinterpret_cast<const void*>(&dispatch_kernel<VB, kDispatchU, kDispatchLP, kDispatchSP>); break;
     MOE_EP_D(16) MOE_EP_D(8) MOE_EP_D(4) MOE_EP_D(2) MOE_EP_D(1)
 #undef MOE_EP_D
     default: return hipErrorInvalidValue;
@@ -412,7 +440,7 @@ hipError_t launch_combine(const CombineKArgs& a, int dtype, int vec_elems, hipSt
   if (sh.grid_x <= 0) return hipSuccess;
   const void* fn = nullptr;
 #define MOE_EP_C(DT, VE) \
-    case VE: fn = reinterpret_cast<const void*>(&combine_kernel<DT, VE, kCombineU, kCombineDB, kCombineNT>); break;
+    case VE: fn = reinterpret_cast<const void*>(&combine_kernel<DT, VE, kCombineU, kCombineDB, kCombineLP, kCombineSP>); break;
   if (dtype == MOE_EP_F32) {
     switch (vec_elems) {
       MOE_EP_C(MOE_EP_F32, 4) MOE_EP_C(MOE_EP_F32, 2) MOE_EP_C(MOE_EP_F32, 1)

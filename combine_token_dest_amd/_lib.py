@@ -45,7 +45,7 @@ class moe_ep_params(Structure):
         ("max_tokens_per_rank", c_int32), ("hidden_size", c_int32),
         ("combine_max_elem_bytes", c_int32), ("hidden_row_bytes", c_int64),
         ("scale_row_bytes", c_int64), ("invalid_expert_id", c_int32),
-        ("enable_rank_mask", c_int32),
+        ("enable_rank_mask", c_int32), ("eplb_stats_bytes", c_int64),
     ]
 
 
@@ -55,6 +55,7 @@ class moe_ep_dispatch_args(Structure):
         ("topk_weights", c_void_p * R), ("local_num_tokens", c_int32 * R),
         ("weights_present", c_uint64), ("scales_present", c_uint64),
         ("runtime_max_tokens_per_rank", c_int32), ("active_rank_mask", c_uint64),
+        ("eplb_local_stats", c_void_p * R), ("eplb_present", c_uint64),
     ]
 
 
@@ -62,6 +63,7 @@ class moe_ep_dispatch_result(Structure):
     _fields_ = [
         ("hidden", c_void_p), ("hidden_scale", c_void_p), ("topk_ids", c_void_p),
         ("topk_weights", c_void_p), ("tokens_per_rank", c_int32), ("num_rows", c_int32),
+        ("eplb_global_stats", c_void_p),
     ]
 
 

@@ -90,6 +90,8 @@ int validate_params(const moe_ep_params* p) {
     return fail(MOE_EP_ERR_INVALID_ARG, "hidden_row_bytes %lld < 1", (long long)p->hidden_row_bytes);
   if (p->scale_row_bytes < 0)
     return fail(MOE_EP_ERR_INVALID_ARG, "scale_row_bytes %lld < 0", (long long)p->scale_row_bytes);
+  if (p->eplb_stats_bytes < 0 || p->eplb_stats_bytes > INT32_MAX)
+    return fail(MOE_EP_ERR_INVALID_ARG, "eplb_stats_bytes %lld outside [0, 2^31)", (long long)p->eplb_stats_bytes);
   // Row and grid indices are 32-bit in the kernels; byte offsets are 64-bit.
   const int64_t rows = (int64_t)p->ep_size * p->max_tokens_per_rank;
   if (rows > (int64_t)1 << 30) return fail(MOE_EP_ERR_INVALID_ARG, "ep_size * capacity too large");
@@ -119,6 +121,8 @@ bool make_layout(const moe_ep_params* p, Layout* L) {
   off += align_up((int64_t)ids, kAlign);
   L->off_combine = off;
   off += align_up((int64_t)cmb, kAlign);
+  L->off_eplb = off;
+  off += align_up((int64_t)p->ep_size * p->eplb_stats_bytes, kAlign);
   L->part_stride = align_up(off, 4096);
   const unsigned __int128 parts = (unsigned __int128)L->part_stride * (unsigned __int128)p->ep_size;
   if (parts > limit) return false;
@@ -273,6 +277,13 @@ int moe_ep_dispatch(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispa
   const bool has_s = sp != 0;
   if (has_s && p.scale_row_bytes == 0)
     return fail(MOE_EP_ERR_INVALID_ARG, "hidden_states_scale passed but scale_row_bytes is 0");
+  const uint64_t ep_present = a->eplb_present & all;
+  if (ep_present != 0 && ep_present != all)
+    return fail(MOE_EP_ERR_INVALID_ARG, "eplb_local_stats passed by some ranks only (mask 0x%llx)",
+                (unsigned long long)ep_present);
+  const bool has_e = ep_present != 0;
+  if (has_e && p.eplb_stats_bytes == 0)
+    return fail(MOE_EP_ERR_INVALID_ARG, "eplb_local_stats passed but eplb_stats_bytes is 0");
 
   DispatchKArgs k;
   std::memset(&k, 0, sizeof(k));
@@ -301,6 +312,17 @@ int moe_ep_dispatch(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispa
     k.scale[s] = has_s ? static_cast<const uint8_t*>(a->hidden_scale[s]) : nullptr;
   }
   const int vec_bytes = (int)pow2_divisor(hidden_align_or, 16);
+  uint64_t eplb_align_or = (uint64_t)p.eplb_stats_bytes;
+  if (has_e) {
+    for (int s = 0; s < ep; ++s) {
+      if (!a->eplb_local_stats[s]) return fail(MOE_EP_ERR_INVALID_ARG, "rank %d: NULL eplb_local_stats", s);
+      eplb_align_or |= reinterpret_cast<uintptr_t>(a->eplb_local_stats[s]);
+      k.eplb[s] = static_cast<const uint8_t*>(a->eplb_local_stats[s]);
+    }
+  }
+  k.off_eplb = h->L.off_eplb;
+  k.eplb_bytes = has_e ? p.eplb_stats_bytes : 0;
+  k.eplb_vec4 = has_e && (eplb_align_or % 4 == 0);
 
   k.ws = h->ws;
   k.route = reinterpret_cast<uint64_t*>(h->ws + h->L.off_route);
@@ -336,6 +358,7 @@ int moe_ep_dispatch(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispa
     results[d].topk_weights = has_w ? reinterpret_cast<float*>(part + h->L.off_weights) : nullptr;
     results[d].tokens_per_rank = tpr;
     results[d].num_rows = ep * tpr;
+    results[d].eplb_global_stats = has_e ? part + h->L.off_eplb : nullptr;
   }
   return ok();
 }

@@ -19,6 +19,7 @@ struct Layout {
   int64_t off_ids;       // [ep*cap, top_k] int32
   int64_t off_weights;   // [ep*cap, top_k] float
   int64_t off_combine;   // [ep*cap, hidden_size * combine_max_elem_bytes]
+  int64_t off_eplb;      // [ep, eplb_stats_bytes]
   int64_t part_stride;   // bytes per rank partition
   int64_t off_route;     // [ep, cap] uint64 destination masks
   int64_t total;         // workspace bytes
@@ -55,6 +56,10 @@ struct DispatchKArgs {
   int32_t invalid_id;
   int32_t has_weights;
   int32_t scale_vec4;                  // scale rows copied as 4-byte words (else bytes)
+  const uint8_t* eplb[kMaxRanks];      // per source rank: its statistics row, or all NULL
+  int64_t off_eplb;
+  int64_t eplb_bytes;                  // 0 when no statistics are gathered
+  int32_t eplb_vec4;                   // statistics copied as 4-byte words (else bytes)
 };
 
 // Kernel arguments of the combine kernel, passed by value.

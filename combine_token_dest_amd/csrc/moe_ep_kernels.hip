@@ -232,14 +232,43 @@ __device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const int r
   }
 }
 
+// Gathers source rank s's expert-load statistics into row s of the
+// [ep, eplb_bytes] statistics region of every rank.
+__device__ __forceinline__ void gather_stats_row(const DispatchKArgs& a, const int s) {
+  const int64_t B = a.eplb_bytes;
+  const int64_t dst_off = a.off_eplb + (int64_t)s * B;
+  if (a.eplb_vec4) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.eplb[s]);
+    for (int64_t c = threadIdx.x; c < B / 4; c += blockDim.x) {
+      const uint32_t x = src[c];
+      for (int d = 0; d < a.ep; ++d)
+        reinterpret_cast<uint32_t*>(a.ws + (int64_t)d * a.part_stride + dst_off)[c] = x;
+    }
+  } else {
+    const uint8_t* src = a.eplb[s];
+    for (int64_t c = threadIdx.x; c < B; c += blockDim.x) {
+      const uint8_t x = src[c];
+      for (int d = 0; d < a.ep; ++d) (a.ws + (int64_t)d * a.part_stride + dst_off)[c] = x;
+    }
+  }
+}
+
 // Grid: x strides over the receive rows r = s*tpr + t (one row per
-// workgroup when the grid is as large as the row count), y = column chunk
-// of the hidden row.
+// workgroup when the grid is as large as the row count), then over one
+// statistics row per source rank when statistics are gathered; y = column
+// chunk of the hidden row.
 template <int VB, int U, int LP, int SP>
 __global__ void __launch_bounds__(kMaxBlock)
 dispatch_kernel(const DispatchKArgs a) {
   const int rows = a.ep * a.tpr;
-  for (int r = blockIdx.x; r < rows; r += gridDim.x) dispatch_row<VB, U, LP, SP>(a, r);
+  const int items = rows + (a.eplb_bytes ? a.ep : 0);
+  for (int r = blockIdx.x; r < items; r += gridDim.x) {
+    if (r < rows) {
+      dispatch_row<VB, U, LP, SP>(a, r);
+    } else if (blockIdx.y == 0) {
+      gather_stats_row(a, r - rows);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -421,7 +450,7 @@ LaunchShape combine_shape(int64_t tokens, int64_t hidden, int vec_elems) {
 }
 
 hipError_t launch_dispatch(const DispatchKArgs& a, int vec_bytes, hipStream_t stream) {
-  const LaunchShape sh = dispatch_shape((int64_t)a.ep * a.tpr, a.hidden_bytes, vec_bytes);
+  const LaunchShape sh = dispatch_shape((int64_t)a.ep * a.tpr + (a.eplb_bytes ? a.ep : 0), a.hidden_bytes, vec_bytes);
   if (sh.grid_x <= 0) return hipSuccess;
   const void* fn;
   switch (vec_bytes) {

@@ -34,6 +34,7 @@ class DispatchResult:
     topk_ids: torch.Tensor                  # int32 [ep*tpr, top_k]
     topk_weights: Optional[torch.Tensor]    # float32 [ep*tpr, top_k] or None
     tokens_per_rank: int
+    eplb_global_stats: Optional[torch.Tensor] = None   # [ep, stats elements]: every rank's stats
 
 
 def _mask_value(mask) -> int:
@@ -60,7 +61,7 @@ class MoEEp:
     def __init__(self, ep_size: int, num_experts: int, top_k: int, max_tokens_per_rank: int,
                  hidden_size: int, *, hidden_row_bytes: Optional[int] = None, scale_row_bytes: int = 0,
                  combine_max_elem_bytes: int = 2, invalid_expert_id: int = -1,
-                 enable_rank_mask: bool = False, device=None):
+                 enable_rank_mask: bool = False, eplb_stats_bytes: int = 0, device=None):
         dev = torch.device("cuda") if device is None else torch.device(device)
         if dev.type != "cuda":
             raise ValueError(f"MoEEp needs a GPU device, got {dev}")
@@ -71,7 +72,7 @@ class MoEEp:
             combine_max_elem_bytes=combine_max_elem_bytes,
             hidden_row_bytes=hidden_row_bytes if hidden_row_bytes is not None else hidden_size * 2,
             scale_row_bytes=scale_row_bytes, invalid_expert_id=invalid_expert_id,
-            enable_rank_mask=1 if enable_rank_mask else 0)
+            enable_rank_mask=1 if enable_rank_mask else 0, eplb_stats_bytes=eplb_stats_bytes)
         nbytes = _lib.moe_ep_workspace_bytes(self.params)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         self._handle = _lib.moe_ep_create(self.params, self.workspace.data_ptr(), nbytes)
@@ -109,8 +110,6 @@ class MoEEp:
                  eplb_local_stats=None, active_rank_mask=None) -> List[DispatchResult]:
         """Send every token to the ranks owning its experts; see
         include/moe_ep.h, moe_ep_dispatch."""
-        if eplb_local_stats is not None:
-            raise NotImplementedError("eplb_local_stats is not supported by this backend")
         if self._handle is None:
             raise RuntimeError("MoEEp has been destroyed")
         p = self.params
@@ -146,6 +145,19 @@ class MoEEp:
                                      f"{p.scale_row_bytes} bytes")
                 sp |= 1 << s
                 a.hidden_scale[s] = _dev_ptr(sc, self.device, f"hidden_states_scale[{s}]") if ns else None
+        ep_present = 0
+        if eplb_local_stats is not None:
+            if len(eplb_local_stats) != ep:
+                raise ValueError(f"expected {ep} per-rank eplb_local_stats")
+            for s in range(ep):
+                st = eplb_local_stats[s]
+                if st is None:
+                    continue
+                if st.numel() * st.element_size() != p.eplb_stats_bytes:
+                    raise ValueError(f"rank {s}: eplb_local_stats must hold {p.eplb_stats_bytes} bytes")
+                ep_present |= 1 << s
+                a.eplb_local_stats[s] = _dev_ptr(st, self.device, f"eplb_local_stats[{s}]")
+        a.eplb_present = ep_present
         a.weights_present = wp
         a.scales_present = sp
         a.runtime_max_tokens_per_rank = -1 if runtime_max_tokens_per_rank is None \
@@ -159,6 +171,9 @@ class MoEEp:
         sdt = None
         if sp:
             sdt = next(x for x in hidden_states_scale if x is not None).dtype
+        edt = None
+        if ep_present:
+            edt = next(x for x in eplb_local_stats if x is not None).dtype
         out = []
         for d in range(ep):
             r = res[d]
@@ -169,7 +184,9 @@ class MoEEp:
                 topk_ids=self._view(r.topk_ids, rows, p.top_k * 4, torch.int32),
                 topk_weights=self._view(r.topk_weights, rows, p.top_k * 4, torch.float32)
                 if r.topk_weights else None,
-                tokens_per_rank=r.tokens_per_rank))
+                tokens_per_rank=r.tokens_per_rank,
+                eplb_global_stats=self._view(r.eplb_global_stats, ep, p.eplb_stats_bytes, edt)
+                if r.eplb_global_stats else None))
         return out
 
     def get_combine_input_buffer(self, rank: int, dtype: torch.dtype) -> torch.Tensor:

@@ -82,6 +82,9 @@ typedef struct moe_ep_params {
   int64_t scale_row_bytes;        /* bytes of one hidden_states_scale row; 0 = no scales */
   int32_t invalid_expert_id;      /* written into every top_k slot of an invalid receive row */
   int32_t enable_rank_mask;       /* nonzero: dispatch/combine accept an active_rank_mask */
+  int64_t eplb_stats_bytes;       /* bytes of one rank's expert-load statistics row, gathered
+                                     by dispatch (MoEEpCommunication, dispatch(),
+                                     eplb_local_stats); 0 = not supported */
 } moe_ep_params;
 
 /* Inputs of one dispatch, per SOURCE rank s < ep_size
@@ -98,6 +101,9 @@ typedef struct moe_ep_dispatch_args {
   int32_t        runtime_max_tokens_per_rank; /* < 0 = None = capacity; else in [max n_s, capacity] */
   uint64_t       active_rank_mask; /* MOE_EP_ALL_RANKS = no mask; else needs enable_rank_mask
                                       and only bits < ep_size */
+  const void*    eplb_local_stats[MOE_EP_MAX_RANKS]; /* device [eplb_stats_bytes] per rank, or NULL */
+  uint64_t       eplb_present;     /* bit s: rank s passed eplb_local_stats.  None or all; needs
+                                      eplb_stats_bytes > 0 */
 } moe_ep_dispatch_args;
 
 /* What destination rank d received: views into its workspace partition,
@@ -109,6 +115,8 @@ typedef struct moe_ep_dispatch_result {
   float*   topk_weights;    /* device [num_rows, top_k], NULL when no weights passed */
   int32_t  tokens_per_rank; /* tpr of this step */
   int32_t  num_rows;        /* ep_size * tokens_per_rank */
+  void*    eplb_global_stats; /* device [ep_size, eplb_stats_bytes]: row s holds rank s's
+                                 eplb_local_stats; NULL when none were passed */
 } moe_ep_dispatch_result;
 
 /* Inputs of one combine (MoEEpCommunication, combine()). */
@@ -149,6 +157,9 @@ MOE_EP_API int moe_ep_create(const moe_ep_params* params, void* workspace, size_
  * t >= n_s) gets invalid_expert_id in all top_k slots and weight 0.0; its
  * hidden and scale bytes are left unspecified.  tpr is
  * runtime_max_tokens_per_rank, or the capacity when it is < 0.
+ * When every rank passes eplb_local_stats, each rank's statistics row is
+ * also gathered into row s of a [ep_size, eplb_stats_bytes] region on every
+ * rank (MoEEpCommunication, dispatch(), eplb_local_stats), in the same launch.
  * Fills results[0 .. ep_size-1] (host array) with views into the workspace.
  * Needs the IDLE state; leaves the handle DISPATCHED.  One kernel launch. */
 MOE_EP_API int moe_ep_dispatch(moe_ep_handle handle, const moe_ep_dispatch_args* args,

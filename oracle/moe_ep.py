@@ -77,6 +77,7 @@ class Params:
     scale_row_bytes: int = 0  # bytes of a dispatched scale row, 0 = no scales
     invalid_expert_id: int = -1
     enable_rank_mask: bool = False
+    eplb_stats_bytes: int = 0   # bytes of one rank's expert-load statistics row
 
     def check(self) -> None:
         if not (1 <= self.ep_size <= MAX_RANKS):
@@ -99,6 +100,7 @@ class RankResult:
     topk_weights: Optional[np.ndarray]    # float32 [ep*tpr, top_k] or None
     tokens_per_rank: int
     valid: np.ndarray                     # bool [ep*tpr]: rows that hold a routed token
+    eplb_global_stats: Optional[np.ndarray] = None   # uint8 [ep, eplb_stats_bytes] or None
 
 
 @dataclass
@@ -186,14 +188,18 @@ class OracleMoEEp:
                  topk_weights: Optional[Sequence[Optional[np.ndarray]]] = None, *,
                  hidden_states_scale: Optional[Sequence[Optional[np.ndarray]]] = None,
                  runtime_max_tokens_per_rank: Optional[int] = None,
-                 active_rank_mask: Optional[int] = None) -> List[RankResult]:
+                 active_rank_mask: Optional[int] = None,
+                 eplb_local_stats: Optional[Sequence[Optional[np.ndarray]]] = None) -> List[RankResult]:
         """Per-rank inputs in, per-rank receive regions out.
 
         ``hidden_states[s]`` is a uint8 ``[n_s, hidden_row_bytes]`` array (rows
         are opaque bytes, quantized or not), ``topk_ids[s]`` an int
         ``[n_s, top_k]`` array, ``topk_weights[s]`` a float32 ``[n_s, top_k]``
         array and ``hidden_states_scale[s]`` a uint8 ``[n_s, scale_row_bytes]``
-        array.
+        array.  ``eplb_local_stats[s]`` (optional, uint8 ``[eplb_stats_bytes]``)
+        is rank s's expert-load statistics row; dispatch all-gathers these
+        (MoEEpCommunication, dispatch(), eplb_local_stats): every rank's
+        result holds all of them, row s from rank s.
         """
         p = self.params
         ep, K = p.ep_size, p.top_k
@@ -217,6 +223,17 @@ class OracleMoEEp:
             raise OracleError("invalid_arg", "hidden_states_scale passed by some ranks only")
         if has_s and p.scale_row_bytes == 0:
             raise OracleError("invalid_arg", "scales passed but scale_row_bytes is 0")
+        has_e = eplb_local_stats is not None and any(x is not None for x in eplb_local_stats)
+        if has_e and any(x is None for x in eplb_local_stats):
+            raise OracleError("invalid_arg", "eplb_local_stats passed by some ranks only")
+        if has_e and p.eplb_stats_bytes == 0:
+            raise OracleError("invalid_arg", "eplb_local_stats passed but eplb_stats_bytes is 0")
+        gathered = None
+        if has_e:
+            # All-gather: row s of every rank's copy is rank s's statistics.
+            gathered = np.empty((ep, p.eplb_stats_bytes), np.uint8)
+            for s in range(ep):
+                gathered[s] = np.asarray(eplb_local_stats[s], np.uint8).reshape(p.eplb_stats_bytes)
 
         # Destination ranks of every token; padding rows (t >= n_s) go nowhere.
         dest_masks = []
@@ -259,7 +276,8 @@ class OracleMoEEp:
                         out_ids[r] = p.invalid_expert_id
                         if has_w:
                             out_w[r] = 0.0
-            results.append(RankResult(out_hidden, out_scale, out_ids, out_w, tpr, valid))
+            results.append(RankResult(out_hidden, out_scale, out_ids, out_w, tpr, valid,
+                                      None if gathered is None else gathered.copy()))
 
         self.record = DispatchRecord(tpr, n, dest_masks, active)
         return results

@@ -34,6 +34,7 @@ class GoldenCase:
     combine_mask: Optional[int]
     expert_output: List[np.ndarray]       # float32, or uint16 bf16 bits
     expect_combine: List[np.ndarray]
+    eplb_local_stats: Optional[List[np.ndarray]] = None
 
 
 def _f32(x):
@@ -62,9 +63,11 @@ def load(path: str) -> GoldenCase:
     else:
         eo = [np.array(cb["expert_output_bits"][d], np.uint16) for d in range(ep)]
         ec = [np.array(g["expect_combine_bits"][s], np.uint16).reshape(-1, hid) for s in range(ep)]
+    es = dd.get("eplb_local_stats")
+    es = None if es is None else [np.array(x, np.uint8) for x in es]
     return GoldenCase(os.path.splitext(os.path.basename(path))[0], p, hidden, ids, w, sc,
                       dd["runtime_max_tokens_per_rank"], dd["active_rank_mask"], g["expect_dispatch"],
-                      dtype, cb["active_rank_mask"], eo, ec)
+                      dtype, cb["active_rank_mask"], eo, ec, es)
 
 
 def all_cases() -> List[GoldenCase]:

@@ -52,6 +52,8 @@ class Case:
     invalid_id: int = -1
     enable_rank_mask: bool = False
     name: str = ""
+    eplb: Optional[List[np.ndarray]] = None     # uint8 [eplb_bytes] per rank
+    eplb_bytes: int = 0
 
     @property
     def n(self):
@@ -68,14 +70,16 @@ def case_from_workload(w: wl.Workload, local_num_tokens=None, seed=None) -> Case
 
 
 def oracle_params(c: Case) -> oracle.Params:
-    return oracle.Params(c.ep, c.E, c.K, c.cap, c.hidden_size, c.H, c.S, c.invalid_id, c.enable_rank_mask)
+    return oracle.Params(c.ep, c.E, c.K, c.cap, c.hidden_size, c.H, c.S, c.invalid_id, c.enable_rank_mask,
+                         c.eplb_bytes)
 
 
 def make_gpu(c: Case, device="cuda"):
     from combine_token_dest_amd import MoEEp
     return MoEEp(c.ep, c.E, c.K, c.cap, c.hidden_size, hidden_row_bytes=c.H, scale_row_bytes=c.S,
                  combine_max_elem_bytes=4 if c.combine_dtype == "f32" else 2,
-                 invalid_expert_id=c.invalid_id, enable_rank_mask=c.enable_rank_mask, device=device)
+                 invalid_expert_id=c.invalid_id, enable_rank_mask=c.enable_rank_mask,
+                 eplb_stats_bytes=c.eplb_bytes, device=device)
 
 
 def to_dev(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -88,6 +92,10 @@ def upload(c: Case, device="cuda"):
     w = None if c.weights is None else [to_dev(x, device) for x in c.weights]
     sc = None if c.scale is None else [to_dev(x, device) for x in c.scale]
     return hid, ids, w, sc
+
+
+def upload_eplb(c: Case, device="cuda"):
+    return None if c.eplb is None else [to_dev(x, device) for x in c.eplb]
 
 
 def combine_inputs_host(c: Case, ores) -> List[np.ndarray]:
@@ -140,6 +148,11 @@ def compare_dispatch(c: Case, gres, ores, tag=""):
         else:
             gs = g.hidden_scale.view(torch.uint8).cpu().numpy().reshape(len(v), c.S)
             np.testing.assert_array_equal(gs[v], o.hidden_scale[v], err_msg=f"{tag} rank {d}: scale bytes")
+        if o.eplb_global_stats is None:
+            assert g.eplb_global_stats is None
+        else:
+            ge = g.eplb_global_stats.view(torch.uint8).cpu().numpy().reshape(c.ep, c.eplb_bytes)
+            np.testing.assert_array_equal(ge, o.eplb_global_stats, err_msg=f"{tag} rank {d}: eplb stats")
 
 
 def compare_combine(c: Case, gout, oout, tag=""):
@@ -165,7 +178,7 @@ def run_step(c: Case, *, zero_copy=True, device="cuda", check=True, moe=None):
     p = oracle_params(c)
     om = oracle.OracleMoEEp(p)
     ores = om.dispatch(c.hidden, c.ids, c.weights, hidden_states_scale=c.scale,
-                       runtime_max_tokens_per_rank=c.rtpr, active_rank_mask=c.mask)
+                       runtime_max_tokens_per_rank=c.rtpr, active_rank_mask=c.mask, eplb_local_stats=c.eplb)
     eo_host = combine_inputs_host(c, ores)
     oout = om.combine(eo_host, c.combine_dtype, active_rank_mask=c.mask)
 
@@ -175,7 +188,7 @@ def run_step(c: Case, *, zero_copy=True, device="cuda", check=True, moe=None):
     hid, ids, w, sc = upload(c, device)
     mask_arg = None if c.mask is None else c.mask
     gres = moe.dispatch(hid, ids, w, hidden_states_scale=sc, runtime_max_tokens_per_rank=c.rtpr,
-                        active_rank_mask=mask_arg)
+                        active_rank_mask=mask_arg, eplb_local_stats=upload_eplb(c, device))
     torch.cuda.synchronize()
     if check:
         compare_dispatch(c, gres, ores, c.name)

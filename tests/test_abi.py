@@ -176,6 +176,28 @@ def test_dispatch_validation(lib):
     _lib.moe_ep_destroy(h)
 
 
+def test_eplb_validation(lib):
+    p = params()
+    h = _lib.moe_ep_create(p, FAKE_WS, _lib.moe_ep_workspace_bytes(p))
+    a = dispatch_args([5, 0, 3, 0])
+    a.eplb_present = 0b1111                                                   # no statistics configured
+    for s in range(4):
+        a.eplb_local_stats[s] = FAKE_WS + 64 * s
+    assert status_of(_lib.moe_ep_dispatch, h, a, 4, 0) == _lib.MOE_EP_ERR_INVALID_ARG
+    _lib.moe_ep_destroy(h)
+    p = params(eplb_stats_bytes=1024)
+    h = _lib.moe_ep_create(p, FAKE_WS, _lib.moe_ep_workspace_bytes(p))
+    a.eplb_present = 0b0111                                                   # some ranks only
+    assert status_of(_lib.moe_ep_dispatch, h, a, 4, 0) == _lib.MOE_EP_ERR_INVALID_ARG
+    a.eplb_present = 0b1111
+    a.eplb_local_stats[2] = None                                              # NULL row
+    assert status_of(_lib.moe_ep_dispatch, h, a, 4, 0) == _lib.MOE_EP_ERR_INVALID_ARG
+    _lib.moe_ep_destroy(h)
+    assert status_of(_lib.moe_ep_workspace_bytes, params(eplb_stats_bytes=-1)) == _lib.MOE_EP_ERR_INVALID_ARG
+    assert _lib.moe_ep_workspace_bytes(params(eplb_stats_bytes=1024)) >= \
+        _lib.moe_ep_workspace_bytes(params()) + 4 * 4 * 1024
+
+
 def test_mask_validation(lib):
     p = params(enable_rank_mask=1)
     h = _lib.moe_ep_create(p, FAKE_WS, _lib.moe_ep_workspace_bytes(p))

@@ -42,6 +42,17 @@ def test_workload_full_size(name):
     parity.run_step(c, zero_copy=True)
 
 
+def test_dsv3_with_expert_load_statistics():
+    """The DeepSeek-V3-shaped round with int32 [256] per-rank statistics gathered."""
+    w = wl.BY_NAME["dsv3"]
+    log("[parity] dsv3 + eplb statistics")
+    c = parity.case_from_workload(w)
+    rng = np.random.default_rng(77)
+    c.eplb = [rng.integers(0, 1000, size=w.num_experts).astype(np.int32).view(np.uint8) for _ in range(w.ep_size)]
+    c.eplb_bytes = w.num_experts * 4
+    parity.run_step(c, zero_copy=True)
+
+
 @pytest.mark.parametrize("name", ["dsv3", "ragged"])
 def test_workload_separate_combine_input(name):
     w = wl.BY_NAME[name]
@@ -73,11 +84,12 @@ def test_golden_on_gpu(case):
     c = Case(p["ep_size"], p["num_experts"], p["top_k"], p["max_tokens_per_rank"], p["hidden_size"],
              p["hidden_row_bytes"], p["scale_row_bytes"], case.hidden, case.topk_ids, case.topk_weights,
              case.scale, None, case.runtime_max_tokens_per_rank, case.active_rank_mask, case.combine_dtype,
-             invalid_id=p["invalid_expert_id"], enable_rank_mask=bool(p["enable_rank_mask"]), name=case.name)
+             invalid_id=p["invalid_expert_id"], enable_rank_mask=bool(p["enable_rank_mask"]), name=case.name,
+             eplb=case.eplb_local_stats, eplb_bytes=p.get("eplb_stats_bytes", 0))
     moe = parity.make_gpu(c)
     hid, ids, w, sc = parity.upload(c)
     res = moe.dispatch(hid, ids, w, hidden_states_scale=sc, runtime_max_tokens_per_rank=c.rtpr,
-                       active_rank_mask=c.mask)
+                       active_rank_mask=c.mask, eplb_local_stats=parity.upload_eplb(c))
     e = case.expect
     for d in range(c.ep):
         assert res[d].tokens_per_rank == e["tokens_per_rank"]
@@ -91,6 +103,9 @@ def test_golden_on_gpu(case):
             gs = res[d].hidden_scale.view(torch.uint8).cpu().numpy().reshape(-1, c.S)
             for r, row in e["scale_valid_rows"][d].items():
                 np.testing.assert_array_equal(gs[int(r)], np.array(row, np.uint8))
+        if "eplb_global_stats" in e:
+            np.testing.assert_array_equal(res[d].eplb_global_stats.cpu().numpy(),
+                                          np.array(e["eplb_global_stats"], np.uint8))
     eo = [parity.host_to_torch(case.expert_output[d], c.combine_dtype) for d in range(c.ep)]
     out = moe.combine(eo, active_rank_mask=case.combine_mask)
     for s in range(c.ep):
@@ -106,7 +121,7 @@ def test_golden_on_gpu(case):
 # Edge cases: shapes, vector widths, masks, ids, empty ranks
 # --------------------------------------------------------------------------
 def random_case(seed, ep, E, K, cap, n, hidden_size, H, S=0, rtpr=None, mask=None, dtype="bf16",
-                weights=True, invalid=-1, id_lo=None, id_hi=None, name=""):
+                weights=True, invalid=-1, id_lo=None, id_hi=None, name="", eplb=0):
     rng = np.random.default_rng(seed)
     lo = 0 if id_lo is None else id_lo
     hi = E if id_hi is None else id_hi
@@ -114,8 +129,9 @@ def random_case(seed, ep, E, K, cap, n, hidden_size, H, S=0, rtpr=None, mask=Non
     hidden = [rng.integers(0, 256, size=(n[s], H)).astype(np.uint8) for s in range(ep)]
     w = [rng.standard_normal((n[s], K)).astype(np.float32) for s in range(ep)] if weights else None
     sc = [rng.integers(0, 256, size=(n[s], S)).astype(np.uint8) for s in range(ep)] if S else None
+    st = [rng.integers(0, 256, size=eplb).astype(np.uint8) for _ in range(ep)] if eplb else None
     return Case(ep, E, K, cap, hidden_size, H, S, hidden, ids, w, sc, None, rtpr, mask, dtype,
-                invalid_id=invalid, enable_rank_mask=mask is not None, name=name)
+                invalid_id=invalid, enable_rank_mask=mask is not None, name=name, eplb=st, eplb_bytes=eplb)
 
 
 EDGE = [
@@ -147,6 +163,12 @@ EDGE = [
     ("all_empty_cap", dict(ep=4, E=8, K=2, cap=6, n=[0, 0, 0, 0], hidden_size=16, H=32)),
     ("all_empty_rtpr0", dict(ep=4, E=8, K=2, cap=6, n=[0, 0, 0, 0], hidden_size=16, H=32, rtpr=0)),
     ("cap0", dict(ep=2, E=2, K=1, cap=0, n=[0, 0], hidden_size=16, H=32)),
+    ("eplb_int32_experts", dict(ep=8, E=64, K=4, cap=20, n=[20, 0, 3, 20, 7, 0, 1, 19], hidden_size=256, H=512,
+                                eplb=64 * 4)),
+    ("eplb_odd_bytes", dict(ep=5, E=10, K=2, cap=6, n=[6, 2, 0, 5, 1], hidden_size=32, H=64, eplb=13)),
+    ("eplb_all_empty_rtpr0", dict(ep=4, E=8, K=2, cap=6, n=[0, 0, 0, 0], hidden_size=16, H=32, rtpr=0, eplb=40)),
+    ("eplb_mask", dict(ep=8, E=64, K=6, cap=40, n=[40, 39, 0, 1, 2, 40, 13, 7], hidden_size=512, H=1024,
+                       mask=0b10110101, eplb=256)),
 ]
 
 

@@ -44,7 +44,7 @@ def test_golden_dispatch_and_combine(case):
     o = OracleMoEEp(p)
     res = o.dispatch(case.hidden, case.topk_ids, case.topk_weights, hidden_states_scale=case.scale,
                      runtime_max_tokens_per_rank=case.runtime_max_tokens_per_rank,
-                     active_rank_mask=case.active_rank_mask)
+                     active_rank_mask=case.active_rank_mask, eplb_local_stats=case.eplb_local_stats)
     e = case.expect
     for d in range(p.ep_size):
         assert res[d].tokens_per_rank == e["tokens_per_rank"]
@@ -56,6 +56,10 @@ def test_golden_dispatch_and_combine(case):
         if "scale_valid_rows" in e:
             for r, row in e["scale_valid_rows"][d].items():
                 np.testing.assert_array_equal(res[d].hidden_scale[int(r)], np.array(row, np.uint8))
+        if "eplb_global_stats" in e:
+            np.testing.assert_array_equal(res[d].eplb_global_stats, np.array(e["eplb_global_stats"], np.uint8))
+        else:
+            assert res[d].eplb_global_stats is None
     out = o.combine(case.expert_output, case.combine_dtype, active_rank_mask=case.combine_mask)
     for s in range(p.ep_size):
         if case.combine_dtype == "f32":
@@ -331,6 +335,23 @@ def test_active_rank_mask_helper():
     assert oracle.active_rank_mask([63]) == 1 << 63
     with pytest.raises(OracleError):
         oracle.active_rank_mask([64])
+
+
+def test_eplb_rules():
+    p, hid, ids, w = _small()
+    stats = [np.arange(6, dtype=np.uint8), np.arange(6, 12, dtype=np.uint8)]
+    with pytest.raises(OracleError) as e:
+        OracleMoEEp(p).dispatch(hid, ids, w, eplb_local_stats=stats)      # no statistics configured
+    assert e.value.kind == "invalid_arg"
+    p.eplb_stats_bytes = 6
+    with pytest.raises(OracleError) as e:
+        OracleMoEEp(p).dispatch(hid, ids, w, eplb_local_stats=[stats[0], None])
+    assert e.value.kind == "invalid_arg"
+    res = OracleMoEEp(p).dispatch(hid, ids, w, eplb_local_stats=stats)
+    for d in range(2):
+        np.testing.assert_array_equal(res[d].eplb_global_stats, np.stack(stats))
+    res = OracleMoEEp(p).dispatch(hid, ids, w)
+    assert res[0].eplb_global_stats is None
 
 
 def test_weights_absent_everywhere_is_allowed():

@@ -56,6 +56,7 @@ class moe_ep_dispatch_args(Structure):
         ("weights_present", c_uint64), ("scales_present", c_uint64),
         ("runtime_max_tokens_per_rank", c_int32), ("active_rank_mask", c_uint64),
         ("eplb_local_stats", c_void_p * R), ("eplb_present", c_uint64),
+        ("local_num_tokens_device", c_void_p),
     ]
 
 

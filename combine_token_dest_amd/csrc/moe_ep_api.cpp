@@ -127,9 +127,10 @@ bool make_layout(const moe_ep_params* p, Layout* L) {
   const unsigned __int128 parts = (unsigned __int128)L->part_stride * (unsigned __int128)p->ep_size;
   if (parts > limit) return false;
   L->off_route = (int64_t)parts;
-  const unsigned __int128 total = parts + (unsigned __int128)align_up((int64_t)(rows * 8), kAlign);
+  L->off_counts = L->off_route + align_up((int64_t)(rows * 8), kAlign);
+  const unsigned __int128 total = (unsigned __int128)L->off_counts + kAlign;
   if (total > limit) return false;
-  L->total = total > 0 ? (int64_t)total : kAlign;   // never a zero-byte workspace
+  L->total = (int64_t)total;
   return true;
 }
 
@@ -145,6 +146,7 @@ struct moe_ep_handle_s {
   int32_t tpr;
   int32_t n[MOE_EP_MAX_RANKS];
   uint64_t mask;       // as passed (MOE_EP_ALL_RANKS = none)
+  bool device_counts;  // the dispatch read its token counts from device memory
 };
 
 extern "C" {
@@ -246,16 +248,22 @@ int moe_ep_dispatch(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispa
   const int ep = p.ep_size;
   if (h->state != kIdle) return fail(MOE_EP_ERR_STATE, "dispatch called before the previous dispatch's combine");
 
+  const bool dev_counts = a->local_num_tokens_device != nullptr;
+  if (dev_counts && !aligned(a->local_num_tokens_device, 4))
+    return fail(MOE_EP_ERR_ALIGN, "local_num_tokens_device not 4-byte aligned");
+  const int32_t tpr = a->runtime_max_tokens_per_rank < 0 ? p.max_tokens_per_rank : a->runtime_max_tokens_per_rank;
+  // With device counts every rank may hold up to tpr tokens when the kernel runs.
+  int32_t host_n[MOE_EP_MAX_RANKS];
   int32_t largest = 0;
   for (int s = 0; s < ep; ++s) {
-    const int32_t n = a->local_num_tokens[s];
+    const int32_t n = dev_counts ? tpr : a->local_num_tokens[s];
     if (n < 0) return fail(MOE_EP_ERR_INVALID_ARG, "rank %d: local_num_tokens %d < 0", s, n);
     if (n > p.max_tokens_per_rank)
       return fail(MOE_EP_ERR_CAPACITY, "rank %d: local_num_tokens %d > capacity %d", s, n,
                   p.max_tokens_per_rank);
+    host_n[s] = n;
     if (n > largest) largest = n;
   }
-  const int32_t tpr = a->runtime_max_tokens_per_rank < 0 ? p.max_tokens_per_rank : a->runtime_max_tokens_per_rank;
   if (tpr > p.max_tokens_per_rank)
     return fail(MOE_EP_ERR_CAPACITY, "runtime_max_tokens_per_rank %d > capacity %d", tpr, p.max_tokens_per_rank);
   if (tpr < largest)
@@ -290,7 +298,7 @@ int moe_ep_dispatch(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispa
   uint64_t hidden_align_or = (uint64_t)p.hidden_row_bytes;
   uint64_t scale_align_or = has_s ? (uint64_t)p.scale_row_bytes : 0;
   for (int s = 0; s < ep; ++s) {
-    const int32_t n = a->local_num_tokens[s];
+    const int32_t n = host_n[s];
     k.n[s] = n;
     if (n == 0) continue;
     if (!a->hidden[s] || !a->topk_ids[s])
@@ -320,6 +328,8 @@ int moe_ep_dispatch(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispa
       k.eplb[s] = static_cast<const uint8_t*>(a->eplb_local_stats[s]);
     }
   }
+  k.dev_n = a->local_num_tokens_device;
+  k.counts = reinterpret_cast<int32_t*>(h->ws + h->L.off_counts);
   k.off_eplb = h->L.off_eplb;
   k.eplb_bytes = has_e ? p.eplb_stats_bytes : 0;
   k.eplb_vec4 = has_e && (eplb_align_or % 4 == 0);
@@ -348,8 +358,9 @@ int moe_ep_dispatch(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispa
 
   h->state = kDispatched;
   h->tpr = tpr;
-  for (int s = 0; s < MOE_EP_MAX_RANKS; ++s) h->n[s] = s < ep ? a->local_num_tokens[s] : 0;
+  for (int s = 0; s < MOE_EP_MAX_RANKS; ++s) h->n[s] = s < ep ? host_n[s] : 0;
   h->mask = a->active_rank_mask;
+  h->device_counts = dev_counts;
   for (int d = 0; d < ep; ++d) {
     uint8_t* part = h->ws + (int64_t)d * h->L.part_stride;
     results[d].hidden = part + h->L.off_hidden;
@@ -422,6 +433,9 @@ int moe_ep_combine(moe_ep_handle h, const moe_ep_combine_args* a, void* stream) 
     k.output[s] = static_cast<uint8_t*>(a->output[s]);
   }
   k.token_start[ep] = total;
+  // After a device-count dispatch, h->n holds tpr for every rank (the most
+  // any rank can have); the kernel reads the counts that dispatch used.
+  k.dev_counts = h->device_counts ? reinterpret_cast<const int32_t*>(h->ws + h->L.off_counts) : nullptr;
   const int vec_elems = (int)(pow2_divisor(align_or, 16) / esz);
   k.route = reinterpret_cast<const uint64_t*>(h->ws + h->L.off_route);
   k.hidden = p.hidden_size;

@@ -22,6 +22,7 @@ struct Layout {
   int64_t off_eplb;      // [ep, eplb_stats_bytes]
   int64_t part_stride;   // bytes per rank partition
   int64_t off_route;     // [ep, cap] uint64 destination masks
+  int64_t off_counts;    // [ep] int32 token counts of the last dispatch (device-count steps)
   int64_t total;         // workspace bytes
 };
 
@@ -60,14 +61,17 @@ struct DispatchKArgs {
   int64_t off_eplb;
   int64_t eplb_bytes;                  // 0 when no statistics are gathered
   int32_t eplb_vec4;                   // statistics copied as 4-byte words (else bytes)
+  const int32_t* dev_n;                // device token counts, or NULL to use n[]
+  int32_t* counts;                     // [ep] counts the kernel used (read by combine)
 };
 
 // Kernel arguments of the combine kernel, passed by value.
 struct CombineKArgs {
   const uint8_t* expert_output[kMaxRanks];  // per rank d: [ep*tpr, hidden]
   uint8_t* output[kMaxRanks];               // per source rank s: [n_s, hidden]
-  int32_t token_start[kMaxRanks + 1];       // prefix sums of n_s
+  int32_t token_start[kMaxRanks + 1];       // prefix sums of n_s (host counts)
   const uint64_t* route;                    // [ep, tpr]
+  const int32_t* dev_counts;                // counts written by dispatch, or NULL to use token_start
   int64_t hidden;                           // elements per row
   int32_t tpr;
   int32_t ep;

@@ -115,7 +115,14 @@ __device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const int r
   const int s = r / a.tpr;
   const int t = r - s * a.tpr;
   const int K = a.top_k;
-  const bool real = t < a.n[s];
+  int ns = a.n[s];
+  if (a.dev_n) {
+    // Device-resident count, clamped to the rows the buffers hold.
+    const int c = a.dev_n[s];
+    ns = c < 0 ? 0 : (c > a.tpr ? a.tpr : c);
+  }
+  if (t == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.counts[s] = ns;
+  const bool real = t < ns;
   const int32_t* __restrict__ idr = a.ids[s] + (int64_t)t * K;
   const int64_t nv = a.hidden_bytes / VB;
   const int64_t per_block = (int64_t)blockDim.x * U;
@@ -331,8 +338,16 @@ template <int DT, int VE, int U, int DB, int LP, int SP>
 __device__ __forceinline__ void combine_token(const CombineKArgs& a, const int b) {
   typedef typename CVec<DT, VE>::type V;
   int s = 0;
-  while (s + 1 < a.ep && b >= a.token_start[s + 1]) ++s;    // uniform scan, ep <= 64
-  const int t = b - a.token_start[s];
+  int t;
+  if (a.dev_counts) {
+    // Slots of every possible token; those past the count dispatch used hold none.
+    s = b / a.tpr;
+    t = b - s * a.tpr;
+    if (t >= a.dev_counts[s]) return;
+  } else {
+    while (s + 1 < a.ep && b >= a.token_start[s + 1]) ++s;    // uniform scan, ep <= 64
+    t = b - a.token_start[s];
+  }
   const int64_t r = (int64_t)s * a.tpr + t;
   const uint64_t m = a.route[r];
   const int64_t nv = a.hidden / VE;
@@ -393,12 +408,13 @@ __device__ __forceinline__ void combine_token(const CombineKArgs& a, const int b
   }
 }
 
-// Grid: x strides over the real tokens (prefix over source ranks), y =
-// column chunk of the row.
+// Grid: x strides over the real tokens (prefix over source ranks), or over
+// all ep*tpr token slots after a dispatch that read device-resident counts;
+// y = column chunk of the row.
 template <int DT, int VE, int U, int DB, int LP, int SP>
 __global__ void __launch_bounds__(kMaxBlock)
 combine_kernel(const CombineKArgs a) {
-  const int tokens = a.token_start[a.ep];
+  const int tokens = a.dev_counts ? a.ep * a.tpr : a.token_start[a.ep];
   for (int b = blockIdx.x; b < tokens; b += gridDim.x) combine_token<DT, VE, U, DB, LP, SP>(a, b);
 }
 
@@ -465,7 +481,7 @@ hipError_t launch_dispatch(const DispatchKArgs& a, int vec_bytes, hipStream_t st
 }
 
 hipError_t launch_combine(const CombineKArgs& a, int dtype, int vec_elems, hipStream_t stream) {
-  const LaunchShape sh = combine_shape(a.token_start[a.ep], a.hidden, vec_elems);
+  const LaunchShape sh = combine_shape(a.dev_counts ? (int64_t)a.ep * a.tpr : a.token_start[a.ep], a.hidden, vec_elems);
   if (sh.grid_x <= 0) return hipSuccess;
   const void* fn = nullptr;
 #define MOE_EP_C(DT, VE) \

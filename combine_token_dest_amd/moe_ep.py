@@ -107,9 +107,16 @@ class MoEEp:
                  topk_weights: Optional[Sequence[Optional[torch.Tensor]]] = None, *,
                  hidden_states_scale: Optional[Sequence[Optional[torch.Tensor]]] = None,
                  runtime_max_tokens_per_rank: Optional[int] = None,
-                 eplb_local_stats=None, active_rank_mask=None) -> List[DispatchResult]:
+                 eplb_local_stats=None, active_rank_mask=None,
+                 local_num_tokens_device: Optional[torch.Tensor] = None) -> List[DispatchResult]:
         """Send every token to the ranks owning its experts; see
-        include/moe_ep.h, moe_ep_dispatch."""
+        include/moe_ep.h, moe_ep_dispatch.
+
+        ``local_num_tokens_device`` (optional int32 ``[ep_size]`` on the GPU)
+        makes the kernels read the token counts when they run, so a captured
+        graph can replay steps with other counts.  Every per-rank buffer must
+        then hold ``tokens_per_rank`` rows (the runtime bound, else the
+        capacity), and so do the combine outputs."""
         if self._handle is None:
             raise RuntimeError("MoEEp has been destroyed")
         p = self.params
@@ -160,6 +167,15 @@ class MoEEp:
         a.eplb_present = ep_present
         a.weights_present = wp
         a.scales_present = sp
+        if local_num_tokens_device is not None:
+            t = local_num_tokens_device
+            if t.dtype != torch.int32 or t.numel() != ep:
+                raise ValueError(f"local_num_tokens_device must be int32 [{ep}]")
+            bound = p.max_tokens_per_rank if runtime_max_tokens_per_rank is None else int(runtime_max_tokens_per_rank)
+            if min(n) < bound:
+                raise ValueError(f"with device token counts every rank's buffers must hold {bound} rows")
+            a.local_num_tokens_device = _dev_ptr(t, self.device, "local_num_tokens_device")
+            n = [bound] * ep
         a.runtime_max_tokens_per_rank = -1 if runtime_max_tokens_per_rank is None \
             else int(runtime_max_tokens_per_rank)
         a.active_rank_mask = _mask_value(active_rank_mask)

@@ -104,6 +104,13 @@ typedef struct moe_ep_dispatch_args {
   const void*    eplb_local_stats[MOE_EP_MAX_RANKS]; /* device [eplb_stats_bytes] per rank, or NULL */
   uint64_t       eplb_present;     /* bit s: rank s passed eplb_local_stats.  None or all; needs
                                       eplb_stats_bytes > 0 */
+  const int32_t* local_num_tokens_device; /* optional device int32 [ep_size]: the token counts,
+                                      read by the kernels when they run (so a captured graph
+                                      replays ragged steps).  When set, local_num_tokens is
+                                      ignored, each count is clamped to [0, tokens_per_rank],
+                                      every rank's hidden / ids / weights / scale buffers must
+                                      hold tokens_per_rank rows, and so must every combine
+                                      output buffer.  NULL = use local_num_tokens. */
 } moe_ep_dispatch_args;
 
 /* What destination rank d received: views into its workspace partition,

@@ -79,3 +79,81 @@ def test_graph_replays_match_oracle(name):
         parity.compare_dispatch(c, res, ores, f"{name} replay {i}")
         parity.compare_combine(c, outs, oout, f"{name} replay {i}")
     moe.destroy()
+
+
+def test_graph_replays_ragged_steps_with_device_counts():
+    """One captured round replays steps whose token counts differ: the counts
+    live in device memory and the kernels read them when they run."""
+    w = wl.BY_NAME["ragged"]
+    cap = w.max_tokens_per_rank
+    log("[graph] capture ragged with device-resident counts")
+    full = parity.case_from_workload(w, local_num_tokens=[cap] * w.ep_size, seed=500)
+    full.rtpr = None
+    moe = parity.make_gpu(full)
+    hid, ids, wts, _ = parity.upload(full)
+    counts = torch.full((w.ep_size,), cap, dtype=torch.int32, device="cuda")
+    rows = w.ep_size * cap
+    eo = [torch.zeros((rows, w.hidden_size), dtype=torch.bfloat16, device="cuda") for _ in range(w.ep_size)]
+    outs = [torch.zeros((cap, w.hidden_size), dtype=torch.bfloat16, device="cuda") for _ in range(w.ep_size)]
+    mask = full.mask
+    moe.dispatch(hid, ids, wts, active_rank_mask=mask, local_num_tokens_device=counts)
+    moe.combine(eo, output=outs, active_rank_mask=mask)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        res = moe.dispatch(hid, ids, wts, active_rank_mask=mask, local_num_tokens_device=counts)
+        moe.combine(eo, output=outs, active_rank_mask=mask)
+    torch.cuda.synchronize()
+
+    steps = [[5, 0, 300, 512, 0, 1, 17, 64], [0] * 8, [512] * 8, [3, 0, 2, 9, 0, 0, 4, 1]]
+    for i, nt in enumerate(steps):
+        log(f"[graph] ragged replay {i} n={nt}")
+        c = parity.case_from_workload(w, local_num_tokens=nt, seed=600 + i)
+        c.rtpr = cap
+        om = oracle.OracleMoEEp(parity.oracle_params(c))
+        ores = om.dispatch(c.hidden, c.ids, c.weights, runtime_max_tokens_per_rank=cap, active_rank_mask=mask)
+        eo_host = parity.combine_inputs_host(c, ores)
+        oout = om.combine(eo_host, "bf16", active_rank_mask=mask)
+        for s in range(w.ep_size):
+            n = nt[s]
+            if n:
+                hid[s][:n].copy_(torch.from_numpy(c.hidden[s]))
+                ids[s][:n].copy_(torch.from_numpy(c.ids[s]))
+                wts[s][:n].copy_(torch.from_numpy(c.weights[s]))
+        counts.copy_(torch.tensor(nt, dtype=torch.int32))
+        for d in range(w.ep_size):
+            eo[d].copy_(parity.host_to_torch(eo_host[d], "bf16"))
+        for o in outs:
+            o.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        parity.compare_dispatch(c, res, ores, f"ragged replay {i}")
+        parity.compare_combine(c, [outs[s][:nt[s]] for s in range(w.ep_size)], oout, f"ragged replay {i}")
+        for s in range(w.ep_size):      # rows past the count are left alone
+            assert (outs[s][nt[s]:].float() == 7.0).all()
+    moe.destroy()
+
+
+def test_device_counts_are_clamped_to_the_buffers():
+    """Counts outside [0, tokens_per_rank] are clamped by the kernels."""
+    w = wl.BY_NAME["tiny"]
+    cap = w.max_tokens_per_rank
+    log("[graph] device counts clamped")
+    full = parity.case_from_workload(w)
+    moe = parity.make_gpu(full)
+    hid, ids, wts, _ = parity.upload(full)
+    counts = torch.tensor([-3, cap + 100, 5, cap], dtype=torch.int32, device="cuda")
+    res = moe.dispatch(hid, ids, wts, local_num_tokens_device=counts)
+    outs = moe.combine([moe.get_combine_input_buffer(d, torch.float32) for d in range(w.ep_size)])
+    torch.cuda.synchronize()
+    nt = [0, cap, 5, cap]
+    c = parity.case_from_workload(w)
+    c.hidden = [h[:n] for h, n in zip(c.hidden, nt)]
+    c.ids = [x[:n] for x, n in zip(c.ids, nt)]
+    c.weights = [x[:n] for x, n in zip(c.weights, nt)]
+    om = oracle.OracleMoEEp(parity.oracle_params(c))
+    ores = om.dispatch(c.hidden, c.ids, c.weights, runtime_max_tokens_per_rank=cap)
+    parity.compare_dispatch(c, res, ores, "clamped")
+    assert [tuple(o.shape) for o in outs] == [(cap, w.hidden_size)] * w.ep_size
+    moe.destroy()

@@ -7,15 +7,17 @@ tensors, one list entry per rank.
 """
 
 from ._lib import (MOE_EP_ALL_RANKS, MOE_EP_BF16, MOE_EP_F32, MOE_EP_MAX_RANKS, MoeEpError,
-                   moe_ep_active_rank_mask, moe_ep_combine, moe_ep_create, moe_ep_destroy,
-                   moe_ep_dispatch, moe_ep_get_combine_input_buffer, moe_ep_is_platform_supported,
-                   moe_ep_last_error, moe_ep_status_string, moe_ep_workspace_bytes)
+                   moe_ep_active_rank_mask, moe_ep_checkpoint_prepare, moe_ep_checkpoint_restore,
+                   moe_ep_combine, moe_ep_create, moe_ep_create_vmm, moe_ep_destroy, moe_ep_dispatch,
+                   moe_ep_get_combine_input_buffer, moe_ep_is_platform_supported, moe_ep_last_error,
+                   moe_ep_status_string, moe_ep_workspace, moe_ep_workspace_bytes)
 from .moe_ep import DispatchResult, MoEEp
 
 __all__ = [
     "MOE_EP_ALL_RANKS", "MOE_EP_BF16", "MOE_EP_F32", "MOE_EP_MAX_RANKS", "MoeEpError",
-    "moe_ep_active_rank_mask", "moe_ep_combine", "moe_ep_create", "moe_ep_destroy",
-    "moe_ep_dispatch", "moe_ep_get_combine_input_buffer", "moe_ep_is_platform_supported",
-    "moe_ep_last_error", "moe_ep_status_string", "moe_ep_workspace_bytes",
+    "moe_ep_active_rank_mask", "moe_ep_checkpoint_prepare", "moe_ep_checkpoint_restore",
+    "moe_ep_combine", "moe_ep_create", "moe_ep_create_vmm", "moe_ep_destroy", "moe_ep_dispatch",
+    "moe_ep_get_combine_input_buffer", "moe_ep_is_platform_supported", "moe_ep_last_error",
+    "moe_ep_status_string", "moe_ep_workspace", "moe_ep_workspace_bytes",
     "DispatchResult", "MoEEp",
 ]

@@ -33,6 +33,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_ep.s
 EXPORTS = [
     "moe_ep_is_platform_supported", "moe_ep_workspace_bytes", "moe_ep_create", "moe_ep_dispatch",
     "moe_ep_get_combine_input_buffer", "moe_ep_combine", "moe_ep_destroy",
+    "moe_ep_create_vmm", "moe_ep_workspace", "moe_ep_checkpoint_prepare", "moe_ep_checkpoint_restore",
     "moe_ep_active_rank_mask", "moe_ep_status_string", "moe_ep_last_error",
 ]
 
@@ -111,6 +112,14 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_ep_combine.restype = c_int
     lib.moe_ep_destroy.argtypes = [c_void_p]
     lib.moe_ep_destroy.restype = c_int
+    lib.moe_ep_create_vmm.argtypes = [POINTER(moe_ep_params), POINTER(c_void_p)]
+    lib.moe_ep_create_vmm.restype = c_int
+    lib.moe_ep_workspace.argtypes = [c_void_p, POINTER(c_void_p), POINTER(c_size_t)]
+    lib.moe_ep_workspace.restype = c_int
+    lib.moe_ep_checkpoint_prepare.argtypes = [c_void_p]
+    lib.moe_ep_checkpoint_prepare.restype = c_int
+    lib.moe_ep_checkpoint_restore.argtypes = [c_void_p]
+    lib.moe_ep_checkpoint_restore.restype = c_int
     lib.moe_ep_active_rank_mask.argtypes = [POINTER(c_int32), c_int32, POINTER(c_uint64)]
     lib.moe_ep_active_rank_mask.restype = c_int
     lib.moe_ep_status_string.argtypes = [c_int]
@@ -173,6 +182,27 @@ def moe_ep_combine(handle: int, args: moe_ep_combine_args, stream: int) -> None:
 
 def moe_ep_destroy(handle: Optional[int]) -> None:
     _check(load().moe_ep_destroy(c_void_p(handle or 0)), "moe_ep_destroy")
+
+
+def moe_ep_create_vmm(params: moe_ep_params) -> int:
+    h = c_void_p(0)
+    _check(load().moe_ep_create_vmm(byref(params), byref(h)), "moe_ep_create_vmm")
+    return h.value
+
+
+def moe_ep_workspace(handle: int):
+    p = c_void_p(0)
+    n = c_size_t(0)
+    _check(load().moe_ep_workspace(c_void_p(handle), byref(p), byref(n)), "moe_ep_workspace")
+    return p.value, n.value
+
+
+def moe_ep_checkpoint_prepare(handle: int) -> None:
+    _check(load().moe_ep_checkpoint_prepare(c_void_p(handle)), "moe_ep_checkpoint_prepare")
+
+
+def moe_ep_checkpoint_restore(handle: int) -> None:
+    _check(load().moe_ep_checkpoint_restore(c_void_p(handle)), "moe_ep_checkpoint_restore")
 
 
 def moe_ep_active_rank_mask(ranks: Sequence[int]) -> int:

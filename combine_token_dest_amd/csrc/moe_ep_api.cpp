@@ -136,7 +136,19 @@ bool make_layout(const moe_ep_params* p, Layout* L) {
 
 }  // namespace
 
+// Workspace mapped by the library with HIP virtual memory management.
+struct VmmWorkspace {
+  bool enabled = false;   // handle made by moe_ep_create_vmm
+  bool mapped = false;    // physical memory currently backs the range
+  bool broken = false;    // a map/unmap failed part-way: the range cannot be reused
+  int device = 0;
+  void* va = nullptr;
+  size_t size = 0;
+  hipMemGenericAllocationHandle_t mem{};
+};
+
 struct moe_ep_handle_s {
+  VmmWorkspace vmm;
   moe_ep_params p;
   Layout L;
   uint8_t* ws;
@@ -148,6 +160,68 @@ struct moe_ep_handle_s {
   uint64_t mask;       // as passed (MOE_EP_ALL_RANKS = none)
   bool device_counts;  // the dispatch read its token counts from device memory
 };
+
+namespace {
+
+hipMemAllocationProp vmm_prop(int device) {
+  hipMemAllocationProp prop{};
+  prop.type = hipMemAllocationTypePinned;
+  prop.location.type = hipMemLocationTypeDevice;
+  prop.location.id = device;
+  return prop;
+}
+
+// Backs the reserved range with a new physical allocation.
+int vmm_map(VmmWorkspace& v) {
+  const hipMemAllocationProp prop = vmm_prop(v.device);
+  hipError_t e = hipMemCreate(&v.mem, v.size, &prop, 0);
+  if (e != hipSuccess) return fail(MOE_EP_ERR_HIP, "hipMemCreate: %s", hipGetErrorString(e));
+  e = hipMemMap(v.va, v.size, 0, v.mem, 0);
+  if (e != hipSuccess) {
+    (void)hipMemRelease(v.mem);
+    return fail(MOE_EP_ERR_HIP, "hipMemMap: %s", hipGetErrorString(e));
+  }
+  hipMemAccessDesc access{};
+  access.location.type = hipMemLocationTypeDevice;
+  access.location.id = v.device;
+  access.flags = hipMemAccessFlagsProtReadWrite;
+  e = hipMemSetAccess(v.va, v.size, &access, 1);
+  if (e != hipSuccess) {
+    (void)hipMemUnmap(v.va, v.size);
+    (void)hipMemRelease(v.mem);
+    return fail(MOE_EP_ERR_HIP, "hipMemSetAccess: %s", hipGetErrorString(e));
+  }
+  v.mapped = true;
+  return MOE_EP_OK;
+}
+
+// Waits for the device, then unmaps and releases the physical allocation.
+int vmm_unmap(VmmWorkspace& v) {
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return fail(MOE_EP_ERR_HIP, "hipDeviceSynchronize: %s", hipGetErrorString(e));
+  e = hipMemUnmap(v.va, v.size);
+  if (e != hipSuccess) {
+    v.broken = true;
+    return fail(MOE_EP_ERR_HIP, "hipMemUnmap: %s", hipGetErrorString(e));
+  }
+  v.mapped = false;
+  e = hipMemRelease(v.mem);
+  if (e != hipSuccess) {
+    v.broken = true;
+    return fail(MOE_EP_ERR_HIP, "hipMemRelease: %s", hipGetErrorString(e));
+  }
+  return MOE_EP_OK;
+}
+
+// dispatch / combine / the combine buffer need a mapped, usable workspace.
+int check_workspace_usable(const moe_ep_handle h) {
+  if (h->vmm.broken) return fail(MOE_EP_ERR_STATE, "the workspace failed to map or unmap; destroy the handle");
+  if (h->vmm.enabled && !h->vmm.mapped)
+    return fail(MOE_EP_ERR_STATE, "the workspace is released for a checkpoint; call moe_ep_checkpoint_restore");
+  return MOE_EP_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -215,8 +289,82 @@ int moe_ep_create(const moe_ep_params* params, void* workspace, size_t workspace
 }
 
 int moe_ep_destroy(moe_ep_handle handle) {
+  if (!handle) return ok();
+  int st = MOE_EP_OK;
+  if (handle->vmm.enabled) {
+    if (handle->vmm.mapped) st = vmm_unmap(handle->vmm);
+    if (!handle->vmm.broken) {
+      const hipError_t e = hipMemAddressFree(handle->vmm.va, handle->vmm.size);
+      if (e != hipSuccess && st == MOE_EP_OK) st = fail(MOE_EP_ERR_HIP, "hipMemAddressFree: %s", hipGetErrorString(e));
+    }
+  }
   delete handle;
+  return st;
+}
+
+int moe_ep_create_vmm(const moe_ep_params* params, moe_ep_handle* out_handle) {
+  if (!out_handle) return fail(MOE_EP_ERR_INVALID_ARG, "out_handle is NULL");
+  int st = validate_params(params);
+  if (st != MOE_EP_OK) return st;
+  Layout L;
+  if (!make_layout(params, &L)) return fail(MOE_EP_ERR_INVALID_ARG, "workspace size overflows");
+  VmmWorkspace v;
+  hipError_t e = hipGetDevice(&v.device);
+  if (e != hipSuccess) return fail(MOE_EP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  int supported = 0;
+  e = hipDeviceGetAttribute(&supported, hipDeviceAttributeVirtualMemoryManagementSupported, v.device);
+  if (e != hipSuccess || !supported)
+    return fail(MOE_EP_ERR_UNSUPPORTED, "device %d has no virtual memory management", v.device);
+  const hipMemAllocationProp prop = vmm_prop(v.device);
+  size_t gran = 0;
+  e = hipMemGetAllocationGranularity(&gran, &prop, hipMemAllocationGranularityRecommended);
+  if (e != hipSuccess || gran == 0)
+    return fail(MOE_EP_ERR_HIP, "hipMemGetAllocationGranularity: %s", hipGetErrorString(e));
+  v.size = (size_t)((L.total + (int64_t)gran - 1) / (int64_t)gran) * gran;
+  e = hipMemAddressReserve(&v.va, v.size, gran, nullptr, 0);
+  if (e != hipSuccess) return fail(MOE_EP_ERR_HIP, "hipMemAddressReserve: %s", hipGetErrorString(e));
+  v.enabled = true;
+  st = vmm_map(v);
+  if (st != MOE_EP_OK) {
+    (void)hipMemAddressFree(v.va, v.size);
+    return st;
+  }
+  moe_ep_handle h = nullptr;
+  st = moe_ep_create(params, v.va, v.size, &h);
+  if (st != MOE_EP_OK) {
+    (void)vmm_unmap(v);
+    (void)hipMemAddressFree(v.va, v.size);
+    return st;
+  }
+  h->vmm = v;
+  *out_handle = h;
   return ok();
+}
+
+int moe_ep_workspace(moe_ep_handle h, void** out_ptr, size_t* out_bytes) {
+  if (!h || !out_ptr || !out_bytes) return fail(MOE_EP_ERR_INVALID_ARG, "NULL handle or output");
+  *out_ptr = h->ws;
+  *out_bytes = h->vmm.enabled ? h->vmm.size : (size_t)h->L.total;
+  return ok();
+}
+
+int moe_ep_checkpoint_prepare(moe_ep_handle h) {
+  if (!h) return fail(MOE_EP_ERR_INVALID_ARG, "NULL handle");
+  if (!h->vmm.enabled) return fail(MOE_EP_ERR_UNSUPPORTED, "the workspace is caller-owned; use moe_ep_create_vmm");
+  if (h->vmm.broken) return fail(MOE_EP_ERR_STATE, "the workspace failed to map or unmap; destroy the handle");
+  if (!h->vmm.mapped) return ok();                      // already released
+  if (h->state != kIdle) return fail(MOE_EP_ERR_STATE, "checkpoint_prepare between a dispatch and its combine");
+  return vmm_unmap(h->vmm);
+}
+
+int moe_ep_checkpoint_restore(moe_ep_handle h) {
+  if (!h) return fail(MOE_EP_ERR_INVALID_ARG, "NULL handle");
+  if (!h->vmm.enabled) return fail(MOE_EP_ERR_UNSUPPORTED, "the workspace is caller-owned; use moe_ep_create_vmm");
+  if (h->vmm.broken) return fail(MOE_EP_ERR_STATE, "the workspace failed to map or unmap; destroy the handle");
+  if (h->vmm.mapped) return ok();                       // nothing to restore
+  const int st = vmm_map(h->vmm);
+  if (st != MOE_EP_OK) h->vmm.broken = true;
+  return st;
 }
 
 int moe_ep_active_rank_mask(const int32_t* ranks, int32_t n, uint64_t* out_mask) {
@@ -246,6 +394,8 @@ int moe_ep_dispatch(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispa
   if (!h || !a || !results) return fail(MOE_EP_ERR_INVALID_ARG, "NULL handle, args or results");
   const moe_ep_params& p = h->p;
   const int ep = p.ep_size;
+  int ust = check_workspace_usable(h);
+  if (ust != MOE_EP_OK) return ust;
   if (h->state != kIdle) return fail(MOE_EP_ERR_STATE, "dispatch called before the previous dispatch's combine");
 
   const bool dev_counts = a->local_num_tokens_device != nullptr;
@@ -376,6 +526,8 @@ int moe_ep_dispatch(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispa
 
 int moe_ep_get_combine_input_buffer(moe_ep_handle h, int32_t rank, int32_t dtype, void** out_ptr) {
   if (!h || !out_ptr) return fail(MOE_EP_ERR_INVALID_ARG, "NULL handle or out_ptr");
+  int ust = check_workspace_usable(h);
+  if (ust != MOE_EP_OK) return ust;
   if (h->state != kDispatched)
     return fail(MOE_EP_ERR_STATE, "the combine input buffer is valid only between dispatch and combine");
   if (rank < 0 || rank >= h->p.ep_size) return fail(MOE_EP_ERR_INVALID_ARG, "rank %d outside [0, %d)", rank, h->p.ep_size);
@@ -392,6 +544,8 @@ int moe_ep_combine(moe_ep_handle h, const moe_ep_combine_args* a, void* stream) 
   if (!h || !a) return fail(MOE_EP_ERR_INVALID_ARG, "NULL handle or args");
   const moe_ep_params& p = h->p;
   const int ep = p.ep_size;
+  int ust = check_workspace_usable(h);
+  if (ust != MOE_EP_OK) return ust;
   if (h->state != kDispatched) return fail(MOE_EP_ERR_STATE, "combine called without a preceding dispatch");
   int st = check_mask(p, a->active_rank_mask);
   if (st != MOE_EP_OK) return st;

@@ -47,6 +47,15 @@ def _mask_value(mask) -> int:
     return int(mask) & MOE_EP_ALL_RANKS
 
 
+class _DeviceBytes:
+    """A device byte range exposed through __cuda_array_interface__, so torch
+    can view memory the library mapped itself (no copy, no ownership)."""
+
+    def __init__(self, ptr: int, nbytes: int):
+        self.__cuda_array_interface__ = {"shape": (nbytes,), "typestr": "|u1", "data": (ptr, False),
+                                         "strides": None, "version": 3}
+
+
 def _dev_ptr(t: torch.Tensor, device: torch.device, what: str) -> int:
     if t.device != device:
         raise ValueError(f"{what} is on {t.device}, expected {device}")
@@ -61,7 +70,8 @@ class MoEEp:
     def __init__(self, ep_size: int, num_experts: int, top_k: int, max_tokens_per_rank: int,
                  hidden_size: int, *, hidden_row_bytes: Optional[int] = None, scale_row_bytes: int = 0,
                  combine_max_elem_bytes: int = 2, invalid_expert_id: int = -1,
-                 enable_rank_mask: bool = False, eplb_stats_bytes: int = 0, device=None):
+                 enable_rank_mask: bool = False, eplb_stats_bytes: int = 0, checkpointable: bool = False,
+                 device=None):
         dev = torch.device("cuda") if device is None else torch.device(device)
         if dev.type != "cuda":
             raise ValueError(f"MoEEp needs a GPU device, got {dev}")
@@ -73,9 +83,19 @@ class MoEEp:
             hidden_row_bytes=hidden_row_bytes if hidden_row_bytes is not None else hidden_size * 2,
             scale_row_bytes=scale_row_bytes, invalid_expert_id=invalid_expert_id,
             enable_rank_mask=1 if enable_rank_mask else 0, eplb_stats_bytes=eplb_stats_bytes)
-        nbytes = _lib.moe_ep_workspace_bytes(self.params)
-        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
-        self._handle = _lib.moe_ep_create(self.params, self.workspace.data_ptr(), nbytes)
+        self.checkpointable = checkpointable
+        if checkpointable:
+            # The library maps the workspace itself (HIP virtual memory), so
+            # its physical memory can be released and re-backed at the same
+            # addresses around a process checkpoint.
+            with torch.cuda.device(self.device):
+                self._handle = _lib.moe_ep_create_vmm(self.params)
+            ptr, nbytes = _lib.moe_ep_workspace(self._handle)
+            self.workspace = torch.as_tensor(_DeviceBytes(ptr, nbytes), device=self.device)
+        else:
+            nbytes = _lib.moe_ep_workspace_bytes(self.params)
+            self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            self._handle = _lib.moe_ep_create(self.params, self.workspace.data_ptr(), nbytes)
         self._ws_base = self.workspace.data_ptr()
         self._tpr = None
         self._n = None
@@ -259,6 +279,19 @@ class MoEEp:
         stream = torch.cuda.current_stream(self.device).cuda_stream
         _lib.moe_ep_combine(self._handle, a, stream)
         return outs
+
+    def checkpoint_prepare(self) -> None:
+        """Release the workspace's physical memory before a process
+        checkpoint; its addresses stay reserved, so graphs captured on it
+        replay after checkpoint_restore().  Only between rounds; a repeat
+        call does nothing.  Workspace views must not be touched until the
+        restore (NVLinkOneSidedAlltoAll, checkpoint_prepare())."""
+        _lib.moe_ep_checkpoint_prepare(self._handle)
+
+    def checkpoint_restore(self) -> None:
+        """Back the workspace with new memory; does nothing when it is
+        mapped (NVLinkOneSidedAlltoAll, checkpoint_restore())."""
+        _lib.moe_ep_checkpoint_restore(self._handle)
 
     def destroy(self) -> None:
         """Release the handle; repeated calls do nothing."""

@@ -191,10 +191,44 @@ MOE_EP_API int moe_ep_get_combine_input_buffer(moe_ep_handle handle, int32_t ran
  * leaves the handle IDLE.  One kernel launch. */
 MOE_EP_API int moe_ep_combine(moe_ep_handle handle, const moe_ep_combine_args* args, void* stream);
 
-/* Releases the handle's host state; the workspace stays the caller's.
- * NULL is a no-op.  Device work already enqueued with the handle must have
- * finished before the workspace is reused (MoEEpCommunication, destroy()). */
+/* Releases the handle's host state; a workspace passed to moe_ep_create
+ * stays the caller's, one made by moe_ep_create_vmm is unmapped and freed
+ * (after waiting for the device).  NULL is a no-op.  Device work already
+ * enqueued with the handle must have finished before a caller-owned
+ * workspace is reused (MoEEpCommunication, destroy()). */
 MOE_EP_API int moe_ep_destroy(moe_ep_handle handle);
+
+/* Creates a handle whose workspace the library maps itself with HIP virtual
+ * memory management on the current device: a reserved virtual address range
+ * backed by one physical allocation.  Only such a handle can release its
+ * physical memory for a process checkpoint while its addresses stay put
+ * (NVLinkOneSidedAlltoAll and CakeAlltoAll, checkpoint_prepare() and
+ * checkpoint_restore()).  ERR_UNSUPPORTED when the device lacks virtual
+ * memory management; ERR_HIP when a mapping call fails (nothing is left
+ * allocated). */
+MOE_EP_API int moe_ep_create_vmm(const moe_ep_params* params, moe_ep_handle* out_handle);
+
+/* Device address and size of the handle's workspace.  For a handle from
+ * moe_ep_create_vmm the address is the same for the handle's whole life,
+ * across checkpoints, but must not be touched while the memory is released. */
+MOE_EP_API int moe_ep_workspace(moe_ep_handle handle, void** out_ptr, size_t* out_bytes);
+
+/* Before a process checkpoint: waits for the device, then unmaps and
+ * releases the workspace's physical memory, keeping its virtual addresses
+ * reserved so that HIP graphs captured on the workspace replay once
+ * moe_ep_checkpoint_restore has backed it again.  Only between rounds
+ * (ERR_STATE after a dispatch without its combine).  A second call does
+ * nothing.  Until the restore, dispatch, combine and
+ * get_combine_input_buffer return ERR_STATE.  ERR_UNSUPPORTED for handles
+ * from moe_ep_create.  If unmapping fails part-way the handle is unusable
+ * (every later call but destroy returns ERR_STATE). */
+MOE_EP_API int moe_ep_checkpoint_prepare(moe_ep_handle handle);
+
+/* After the checkpoint: backs the reserved addresses with new physical
+ * memory (contents undefined; the workspace needs no initialisation).  Does
+ * nothing when the workspace is mapped.  If mapping fails part-way the
+ * handle is unusable, as above. */
+MOE_EP_API int moe_ep_checkpoint_restore(moe_ep_handle handle);
 
 /* Bitmask with bit r set for each of the n listed ranks, all in [0, 64)
  * (NVLinkOneSidedAlltoAll, active_rank_mask()).  ERR_MASK for a rank out of

@@ -74,12 +74,12 @@ def oracle_params(c: Case) -> oracle.Params:
                          c.eplb_bytes)
 
 
-def make_gpu(c: Case, device="cuda"):
+def make_gpu(c: Case, device="cuda", checkpointable=False):
     from combine_token_dest_amd import MoEEp
     return MoEEp(c.ep, c.E, c.K, c.cap, c.hidden_size, hidden_row_bytes=c.H, scale_row_bytes=c.S,
                  combine_max_elem_bytes=4 if c.combine_dtype == "f32" else 2,
                  invalid_expert_id=c.invalid_id, enable_rank_mask=c.enable_rank_mask,
-                 eplb_stats_bytes=c.eplb_bytes, device=device)
+                 eplb_stats_bytes=c.eplb_bytes, checkpointable=checkpointable, device=device)
 
 
 def to_dev(a: np.ndarray, device="cuda") -> torch.Tensor:

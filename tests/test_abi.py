@@ -198,6 +198,18 @@ def test_eplb_validation(lib):
         _lib.moe_ep_workspace_bytes(params()) + 4 * 4 * 1024
 
 
+def test_checkpoint_needs_a_library_mapped_workspace(lib):
+    p = params()
+    h = _lib.moe_ep_create(p, FAKE_WS, _lib.moe_ep_workspace_bytes(p))
+    assert status_of(_lib.moe_ep_checkpoint_prepare, h) == _lib.MOE_EP_ERR_UNSUPPORTED
+    assert status_of(_lib.moe_ep_checkpoint_restore, h) == _lib.MOE_EP_ERR_UNSUPPORTED
+    ptr, n = _lib.moe_ep_workspace(h)
+    assert ptr == FAKE_WS and n == _lib.moe_ep_workspace_bytes(p)
+    _lib.moe_ep_destroy(h)
+    assert status_of(_lib.moe_ep_checkpoint_prepare, None) == _lib.MOE_EP_ERR_INVALID_ARG
+    assert status_of(_lib.moe_ep_create_vmm, params(ep_size=0)) == _lib.MOE_EP_ERR_INVALID_ARG
+
+
 def test_mask_validation(lib):
     p = params(enable_rank_mask=1)
     h = _lib.moe_ep_create(p, FAKE_WS, _lib.moe_ep_workspace_bytes(p))

@@ -44,7 +44,8 @@ template <> struct Bytes<4> { typedef uint32_t type; };
 template <> struct Bytes<2> { typedef uint16_t type; };
 template <> struct Bytes<1> { typedef uint8_t type; };
 
-constexpr int kMaxBlock = 512;
+constexpr int kMaxBlock = 512;          // dispatch workgroups
+constexpr int kMaxCombineBlock = 1024;  // combine workgroups (one whole row)
 constexpr int64_t kMaxGridY = 65535;   // chunks beyond this are looped over inside a workgroup
 
 __device__ __forceinline__ int expert_owner(const OwnerDiv& od, uint32_t e) {
@@ -260,21 +261,20 @@ __device__ __forceinline__ void gather_stats_row(const DispatchKArgs& a, const i
   }
 }
 
-// Grid: x strides over the receive rows r = s*tpr + t (one row per
-// workgroup when the grid is as large as the row count), then over one
-// statistics row per source rank when statistics are gathered; y = column
-// chunk of the hidden row.
+// Grid: x = receive row r = s*tpr + t, then one statistics row per source
+// rank when statistics are gathered; y = column chunk of the hidden row.
 template <int VB, int U, int LP, int SP>
 __global__ void __launch_bounds__(kMaxBlock)
 dispatch_kernel(const DispatchKArgs a) {
+  // One workgroup per item (no grid-stride loop: a store of one item could
+  // then alias the next item's loads, which keeps the compiler from using
+  // scalar loads for the uniform ones).
   const int rows = a.ep * a.tpr;
-  const int items = rows + (a.eplb_bytes ? a.ep : 0);
-  for (int r = blockIdx.x; r < items; r += gridDim.x) {
-    if (r < rows) {
-      dispatch_row<VB, U, LP, SP>(a, r);
-    } else if (blockIdx.y == 0) {
-      gather_stats_row(a, r - rows);
-    }
+  const int r = blockIdx.x;
+  if (r < rows) {
+    dispatch_row<VB, U, LP, SP>(a, r);
+  } else if (blockIdx.y == 0) {
+    gather_stats_row(a, r - rows);
   }
 }
 
@@ -345,7 +345,11 @@ __device__ __forceinline__ void combine_token(const CombineKArgs& a, const int b
     t = b - s * a.tpr;
     if (t >= a.dev_counts[s]) return;
   } else {
-    while (s + 1 < a.ep && b >= a.token_start[s + 1]) ++s;    // uniform scan, ep <= 64
+    // Source rank of token b: the last s with token_start[s] <= b (binary
+    // search over the prefix, ep <= 64; empty ranks repeat a start value and
+    // are skipped because the last such s is taken).
+    for (int step = 32; step > 0; step >>= 1)
+      if (s + step < a.ep && b >= a.token_start[s + step]) s += step;
     t = b - a.token_start[s];
   }
   const int64_t r = (int64_t)s * a.tpr + t;
@@ -408,50 +412,57 @@ __device__ __forceinline__ void combine_token(const CombineKArgs& a, const int b
   }
 }
 
-// Grid: x strides over the real tokens (prefix over source ranks), or over
-// all ep*tpr token slots after a dispatch that read device-resident counts;
-// y = column chunk of the row.
+// Grid: x = real token (prefix over source ranks), or one of all ep*tpr
+// token slots after a dispatch that read device-resident counts; y = column
+// chunk of the row.
 template <int DT, int VE, int U, int DB, int LP, int SP>
-__global__ void __launch_bounds__(kMaxBlock)
+__global__ void __launch_bounds__(kMaxCombineBlock)
 combine_kernel(const CombineKArgs a) {
-  const int tokens = a.dev_counts ? a.ep * a.tpr : a.token_start[a.ep];
-  for (int b = blockIdx.x; b < tokens; b += gridDim.x) combine_token<DT, VE, U, DB, LP, SP>(a, b);
+  // One workgroup per token slot, no grid-stride loop: with stores ahead of
+  // it in the same workgroup the route-mask load could not be a scalar load.
+  combine_token<DT, VE, U, DB, LP, SP>(a, blockIdx.x);
 }
 
-int round_block(int64_t threads) {
+int round_block(int64_t threads, int max_block) {
   int64_t b = (threads + 63) / 64 * 64;
   if (b < 64) b = 64;
-  if (b > kMaxBlock) b = kMaxBlock;
+  if (b > max_block) b = max_block;
   return (int)b;
 }
 
 }  // namespace
 
-// Launch configurations, chosen by timing variants on MI355X with the
-// DeepSeek-V3-shaped round (ep 8, 128 tokens per rank, 14 KiB rows) and the
-// 32-rank, 8 KiB-row round, rotating over enough workspaces that the 256 MB
-// MALL holds none of the data between uses:
+// Launch configurations, chosen by timing variants on MI355X in the same
+// alternation the bench uses (8 workspaces rotated so the 256 MB MALL holds
+// none of the data between uses; 8 dispatches then 8 combines) with the
+// DeepSeek-V3-shaped round (ep 8, 128 tokens per rank, 14 KiB rows):
 //  - dispatch: 8 vectors of 16 B per thread and up to 128 threads, so one
-//    workgroup carries up to 16 KiB of a row.
-//  - combine: 2 column vectors per thread, destination rows loaded 4 at a
-//    time, up to 512 threads (a whole 14 KiB bf16 row per workgroup).
+//    workgroup carries up to 16 KiB of a row.  All waves of a workgroup
+//    store a destination row before moving to the next: interleaving the
+//    destinations per vector halved throughput, and staggering the order
+//    across waves, blocked lane mappings, several rows per workgroup or
+//    1-wave workgroups were all 2-10% slower.
+//  - combine: one column vector per thread, a whole row per workgroup (up to
+//    1024 threads), all (up to 8) destination rows loaded in one batch: 5%
+//    faster than 2 vectors x 4 rows per batch.
 //  - nontemporal loads and stores in both: cached combine loads were ~40%
 //    slower, and sc1 (or sc0 sc1) dispatch stores ~8% slower.
 //  Capping the grid below one workgroup per row (persistent loops) was
-//  slower for both kernels.
+//  slower for both kernels, and a grid-stride loop alone cost combine 15%
+//  (its route-mask load became a vector load).
 constexpr int kDispatchU = 8;
 constexpr int kDispatchBlock = 128;
 constexpr int kDispatchLP = kCpNt;
 constexpr int kDispatchSP = kCpNt;
-constexpr int kCombineU = 2;
-constexpr int kCombineDB = 4;
-constexpr int kCombineBlock = 512;
+constexpr int kCombineU = 1;
+constexpr int kCombineDB = 8;
+constexpr int kCombineBlock = 1024;
 constexpr int kCombineLP = kCpNt;
 constexpr int kCombineSP = kCpNt;
 
 LaunchShape dispatch_shape(int64_t rows, int64_t hidden_bytes, int vec_bytes) {
   const int64_t nv = hidden_bytes / vec_bytes;
-  const int block = round_block(std::min<int64_t>(kDispatchBlock, (nv + kDispatchU - 1) / kDispatchU));
+  const int block = round_block(std::min<int64_t>(kDispatchBlock, (nv + kDispatchU - 1) / kDispatchU), kMaxBlock);
   const int64_t per_block = (int64_t)block * kDispatchU;
   const int64_t chunks = std::min<int64_t>(kMaxGridY, std::max<int64_t>(1, (nv + per_block - 1) / per_block));
   return LaunchShape{(int)rows, (int)chunks, block};
@@ -459,7 +470,7 @@ LaunchShape dispatch_shape(int64_t rows, int64_t hidden_bytes, int vec_bytes) {
 
 LaunchShape combine_shape(int64_t tokens, int64_t hidden, int vec_elems) {
   const int64_t nv = hidden / vec_elems;
-  const int block = round_block(std::min<int64_t>(kCombineBlock, (nv + kCombineU - 1) / kCombineU));
+  const int block = round_block(std::min<int64_t>(kCombineBlock, (nv + kCombineU - 1) / kCombineU), kMaxCombineBlock);
   const int64_t per_block = (int64_t)block * kCombineU;
   const int64_t chunks = std::min<int64_t>(kMaxGridY, std::max<int64_t>(1, (nv + per_block - 1) / per_block));
   return LaunchShape{(int)tokens, (int)chunks, block};

@@ -90,14 +90,15 @@ def destination_masks(w, inp):
 # one instance: workspace + inputs + outputs at their own addresses
 # ---------------------------------------------------------------------------
 class Instance:
-    def __init__(self, w, inp, dev_inputs, device):
+    def __init__(self, w, inp, dev_inputs, device, order="auto"):
         import torch
         from combine_token_dest_amd import MoEEp, _lib
         self.w = w
         self.moe = MoEEp(w.ep_size, w.num_experts, w.top_k, w.max_tokens_per_rank, w.hidden_size,
                          hidden_row_bytes=w.hidden_row_bytes, scale_row_bytes=w.scale_row_bytes,
                          combine_max_elem_bytes=w.combine_elem_bytes,
-                         enable_rank_mask=inp.active_rank_mask is not None, device=device)
+                         enable_rank_mask=inp.active_rank_mask is not None, dispatch_order=order,
+                         device=device)
         hid, ids, wts, scl = [[t.clone() for t in lst] if lst is not None else None for lst in dev_inputs[:4]]
         self.inputs = (hid, ids, wts, scl)
         self.cdtype = torch.float32 if w.combine_dtype == "f32" else torch.bfloat16
@@ -109,6 +110,7 @@ class Instance:
         res = self.moe.dispatch(hid, ids, wts, hidden_states_scale=scl, runtime_max_tokens_per_rank=rtpr,
                                 active_rank_mask=mask)
         self.tpr = res[0].tokens_per_rank
+        self.order = self.moe.last_dispatch_order
         values = dev_inputs[4]
         for d in range(w.ep_size):
             buf = self.moe.get_combine_input_buffer(d, self.cdtype)
@@ -247,8 +249,15 @@ class HipEvents:
 
 
 def kernel_source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of the kernel source with comments and whitespace removed,
+    so the PMC traffic figures stay tied to the code they were taken on."""
+    import re
+    with open(KERNEL_SOURCE) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    src = " ".join(src.split())
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
 def read_traffic(workload, kernel):
@@ -261,7 +270,7 @@ def read_traffic(workload, kernel):
     val = None
     for line in open(path):
         parts = line.split()
-        if len(parts) >= 2 and parts[0] == "kernel_source_sha256:":
+        if len(parts) >= 2 and parts[0] == "kernel_code_sha256:":
             src_hash = parts[1]
         if len(parts) >= 3 and parts[0] == "traffic_bytes_per_launch:" and parts[1] == kernel:
             val = float(parts[2])
@@ -277,6 +286,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--instances", type=int, default=8)
+    ap.add_argument("--dispatch-order", default="auto", choices=["auto", "source", "destination"],
+                    help="copy order of the dispatch kernel (the library picks by shape under auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -315,7 +326,7 @@ def main():
     dev_inputs = (dev_hidden, dev_ids, dev_w, dev_s, dev_vals)
 
     log(f"[bench] building {args.instances} instances")
-    insts = [Instance(w, inp, dev_inputs, device) for _ in range(args.instances)]
+    insts = [Instance(w, inp, dev_inputs, device, args.dispatch_order) for _ in range(args.instances)]
     del dev_vals
     torch.cuda.synchronize()
     tpr = insts[0].tpr
@@ -383,8 +394,10 @@ def main():
     d_us = float((d_ms * w_g).sum() / w_g.sum() * 1e3)
     c_us = float((c_ms * w_g).sum() / w_g.sum() * 1e3)
     d_gbs, c_gbs = b_d / (d_us * 1e-6) / 1e9, b_c / (c_us * 1e-6) / 1e9
-    dominant = "dispatch_kernel" if d_us >= c_us else "combine_kernel"
-    dom_bytes, dom_us, dom_gbs = (b_d, d_us, d_gbs) if dominant == "dispatch_kernel" else (b_c, c_us, c_gbs)
+    # kernel names as rocprofv3 lists them (template arguments aside)
+    dname = "dispatch_dst_kernel" if insts[0].order == "destination" else "dispatch_kernel"
+    dominant = dname if d_us >= c_us else "combine_kernel"
+    dom_bytes, dom_us, dom_gbs = (b_d, d_us, d_gbs) if dominant == dname else (b_c, c_us, c_gbs)
     traffic = read_traffic(w.name, dominant)
 
     copy_info = None
@@ -428,7 +441,7 @@ def main():
                                f"num_experts={w.num_experts}, top_k={w.top_k}",
                    "ep_size": w.ep_size, "tokens_per_rank": tpr, "hidden": w.hidden_size,
                    "num_experts": w.num_experts, "top_k": w.top_k, "row_format": w.row_format,
-                   "instances_rotated": I, "seed": w.seed},
+                   "instances_rotated": I, "seed": w.seed, "dispatch_order": insts[0].order},
         "us_per_round": round(ms_step * 1e3, 2),
         "us_per_round_kernels": round(d_us + c_us, 2),
         "timing": "kernel times from fence-free HIP events around runs of I back-to-back launches",
@@ -437,7 +450,7 @@ def main():
         "bytes_per_round": bytes_round,
         "routed_pairs": P, "tokens": N, "receive_rows": R,
         "kernels": {
-            "dispatch_kernel": {"us_mean": round(d_us, 3), "us_p10": round(float(np.percentile(d_ms, 10)) * 1e3, 3),
+            dname: {"us_mean": round(d_us, 3), "us_p10": round(float(np.percentile(d_ms, 10)) * 1e3, 3),
                                 "us_p50": round(float(np.median(d_ms)) * 1e3, 3),
                                 "us_p90": round(float(np.percentile(d_ms, 90)) * 1e3, 3),
                                 "bytes": b_d, "GB/s": round(d_gbs, 1)},
@@ -452,7 +465,7 @@ def main():
                      "traffic": traffic, "algorithmic_bytes_per_launch": dom_bytes,
                      "us_per_launch": round(dom_us, 3)},
         "cpu_baseline": cpu,
-        "kernel_source_sha256": kernel_source_hash(),
+        "kernel_code_sha256": kernel_source_hash(),
     }
     if copy_info:
         out["copy_1GiB"] = copy_info

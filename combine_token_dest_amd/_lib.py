@@ -27,6 +27,10 @@ MOE_EP_ERR_UNSUPPORTED = -7
 MOE_EP_F32 = 0
 MOE_EP_BF16 = 1
 
+MOE_EP_ORDER_AUTO = 0
+MOE_EP_ORDER_SOURCE_ROW = 1
+MOE_EP_ORDER_DESTINATION = 2
+
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_ep.so")
 
 # The exported symbols, in header order.
@@ -47,6 +51,7 @@ class moe_ep_params(Structure):
         ("combine_max_elem_bytes", c_int32), ("hidden_row_bytes", c_int64),
         ("scale_row_bytes", c_int64), ("invalid_expert_id", c_int32),
         ("enable_rank_mask", c_int32), ("eplb_stats_bytes", c_int64),
+        ("dispatch_order", c_int32),
     ]
 
 
@@ -65,7 +70,7 @@ class moe_ep_dispatch_result(Structure):
     _fields_ = [
         ("hidden", c_void_p), ("hidden_scale", c_void_p), ("topk_ids", c_void_p),
         ("topk_weights", c_void_p), ("tokens_per_rank", c_int32), ("num_rows", c_int32),
-        ("eplb_global_stats", c_void_p),
+        ("eplb_global_stats", c_void_p), ("dispatch_order", c_int32),
     ]
 
 

@@ -90,6 +90,8 @@ int validate_params(const moe_ep_params* p) {
     return fail(MOE_EP_ERR_INVALID_ARG, "hidden_row_bytes %lld < 1", (long long)p->hidden_row_bytes);
   if (p->scale_row_bytes < 0)
     return fail(MOE_EP_ERR_INVALID_ARG, "scale_row_bytes %lld < 0", (long long)p->scale_row_bytes);
+  if (p->dispatch_order < MOE_EP_ORDER_AUTO || p->dispatch_order > MOE_EP_ORDER_DESTINATION)
+    return fail(MOE_EP_ERR_INVALID_ARG, "dispatch_order %d unknown", p->dispatch_order);
   if (p->eplb_stats_bytes < 0 || p->eplb_stats_bytes > INT32_MAX)
     return fail(MOE_EP_ERR_INVALID_ARG, "eplb_stats_bytes %lld outside [0, 2^31)", (long long)p->eplb_stats_bytes);
   // Row and grid indices are 32-bit in the kernels; byte offsets are 64-bit.
@@ -503,6 +505,8 @@ int moe_ep_dispatch(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispa
   k.invalid_id = p.invalid_expert_id;
   k.has_weights = has_w ? 1 : 0;
 
+  if (!plan_dispatch(k, vec_bytes, p.dispatch_order))
+    return fail(MOE_EP_ERR_INVALID_ARG, "destination-order dispatch grid too large for this step");
   const hipError_t e = launch_dispatch(k, vec_bytes, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MOE_EP_ERR_HIP, "dispatch launch failed: %s", hipGetErrorString(e));
 
@@ -520,6 +524,7 @@ int moe_ep_dispatch(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispa
     results[d].tokens_per_rank = tpr;
     results[d].num_rows = ep * tpr;
     results[d].eplb_global_stats = has_e ? part + h->L.off_eplb : nullptr;
+    results[d].dispatch_order = k.order;
   }
   return ok();
 }

@@ -63,6 +63,13 @@ struct DispatchKArgs {
   int32_t eplb_vec4;                   // statistics copied as 4-byte words (else bytes)
   const int32_t* dev_n;                // device token counts, or NULL to use n[]
   int32_t* counts;                     // [ep] counts the kernel used (read by combine)
+  int32_t order;                       // MOE_EP_ORDER_SOURCE_ROW or MOE_EP_ORDER_DESTINATION
+  // Destination-major order: rows per block on one XCD, blocks per XCD,
+  // column chunks per row, and the number of (destination, row, chunk) items.
+  int32_t dm_block_rows;
+  int32_t dm_blocks;
+  int32_t dm_chunks;
+  int64_t dm_items;
 };
 
 // Kernel arguments of the combine kernel, passed by value.
@@ -83,8 +90,13 @@ struct LaunchShape {
   int block;    // threads per workgroup
 };
 
-// Enqueue one dispatch kernel.  vec_bytes in {16, 8, 4, 2, 1} must divide
-// hidden_bytes and every hidden row pointer.
+// Fills a.order and the destination-major fields for a step: `requested` is
+// the params' dispatch_order.  Returns false when the destination order was
+// asked for but its grid would not fit.
+bool plan_dispatch(DispatchKArgs& a, int vec_bytes, int requested);
+
+// Enqueue one dispatch kernel (after plan_dispatch).  vec_bytes in
+// {16, 8, 4, 2, 1} must divide hidden_bytes and every hidden row pointer.
 hipError_t launch_dispatch(const DispatchKArgs& a, int vec_bytes, hipStream_t stream);
 
 // Enqueue one combine kernel over a.token_start[ep] tokens.  vec_elems must

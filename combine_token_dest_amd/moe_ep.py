@@ -64,6 +64,15 @@ def _dev_ptr(t: torch.Tensor, device: torch.device, what: str) -> int:
     return t.data_ptr()
 
 
+# Copy order of the dispatch kernel (both give identical results): "source"
+# walks the source rows once and writes each to all its destinations;
+# "destination" writes each destination's rows as one sweep and re-reads the
+# source rows from L2; "auto" lets the library choose from the shape.
+_ORDERS = {"auto": _lib.MOE_EP_ORDER_AUTO, "source": _lib.MOE_EP_ORDER_SOURCE_ROW,
+           "destination": _lib.MOE_EP_ORDER_DESTINATION}
+_ORDER_NAMES = {v: k for k, v in _ORDERS.items()}
+
+
 class MoEEp:
     """One EP group of ``ep_size`` logical ranks on one GPU."""
 
@@ -71,7 +80,7 @@ class MoEEp:
                  hidden_size: int, *, hidden_row_bytes: Optional[int] = None, scale_row_bytes: int = 0,
                  combine_max_elem_bytes: int = 2, invalid_expert_id: int = -1,
                  enable_rank_mask: bool = False, eplb_stats_bytes: int = 0, checkpointable: bool = False,
-                 device=None):
+                 dispatch_order: str = "auto", device=None):
         dev = torch.device("cuda") if device is None else torch.device(device)
         if dev.type != "cuda":
             raise ValueError(f"MoEEp needs a GPU device, got {dev}")
@@ -82,7 +91,8 @@ class MoEEp:
             combine_max_elem_bytes=combine_max_elem_bytes,
             hidden_row_bytes=hidden_row_bytes if hidden_row_bytes is not None else hidden_size * 2,
             scale_row_bytes=scale_row_bytes, invalid_expert_id=invalid_expert_id,
-            enable_rank_mask=1 if enable_rank_mask else 0, eplb_stats_bytes=eplb_stats_bytes)
+            enable_rank_mask=1 if enable_rank_mask else 0, eplb_stats_bytes=eplb_stats_bytes,
+            dispatch_order=_ORDERS[dispatch_order] if isinstance(dispatch_order, str) else int(dispatch_order))
         self.checkpointable = checkpointable
         if checkpointable:
             # The library maps the workspace itself (HIP virtual memory), so
@@ -97,6 +107,7 @@ class MoEEp:
             self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
             self._handle = _lib.moe_ep_create(self.params, self.workspace.data_ptr(), nbytes)
         self._ws_base = self.workspace.data_ptr()
+        self.last_dispatch_order = None
         self._tpr = None
         self._n = None
         self._hidden_dtype = None
@@ -202,6 +213,8 @@ class MoEEp:
         stream = torch.cuda.current_stream(self.device).cuda_stream
         res = _lib.moe_ep_dispatch(self._handle, a, ep, stream)
         self._tpr = res[0].tokens_per_rank if ep else 0
+        # the copy order the library chose for this step ("source" / "destination")
+        self.last_dispatch_order = _ORDER_NAMES.get(res[0].dispatch_order if ep else 0)
         self._n = n
         hdt = hidden_states[0].dtype
         sdt = None

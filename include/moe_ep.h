@@ -62,6 +62,25 @@ typedef enum moe_ep_status {
   MOE_EP_ERR_UNSUPPORTED = -7   /* not a gfx950 device */
 } moe_ep_status;
 
+/* Order in which dispatch writes the receive rows (moe_ep_params.dispatch_order).
+ * Both write the same bytes; they differ only in speed:
+ *  SOURCE_ROW:  a workgroup reads one token row once and writes it to every
+ *               destination in turn (best for large groups and fan-out).
+ *  DESTINATION: a workgroup writes one (destination, row) pair; rows are
+ *               pinned to XCDs so the other destinations' re-reads of a row
+ *               hit that XCD's L2, and each destination's region is written
+ *               as one sequential sweep (best for decode-sized groups).
+ *  AUTO:        DESTINATION when ep_size <= 16 and ep_size^2 * tokens_per_rank
+ *               <= 16384, else SOURCE_ROW.
+ * An explicit DESTINATION request whose grid would pass 2^31 - 1 workgroups
+ * makes moe_ep_dispatch fail with MOE_EP_ERR_INVALID_ARG (nothing launched);
+ * AUTO then takes SOURCE_ROW instead. */
+typedef enum moe_ep_dispatch_order {
+  MOE_EP_ORDER_AUTO = 0,
+  MOE_EP_ORDER_SOURCE_ROW = 1,
+  MOE_EP_ORDER_DESTINATION = 2
+} moe_ep_dispatch_order;
+
 /* Element type of combine's input and output rows (both use the same one). */
 typedef enum moe_ep_dtype {
   MOE_EP_F32 = 0,
@@ -85,6 +104,7 @@ typedef struct moe_ep_params {
   int64_t eplb_stats_bytes;       /* bytes of one rank's expert-load statistics row, gathered
                                      by dispatch (MoEEpCommunication, dispatch(),
                                      eplb_local_stats); 0 = not supported */
+  int32_t dispatch_order;         /* moe_ep_dispatch_order; 0 = AUTO */
 } moe_ep_params;
 
 /* Inputs of one dispatch, per SOURCE rank s < ep_size
@@ -124,6 +144,8 @@ typedef struct moe_ep_dispatch_result {
   int32_t  num_rows;        /* ep_size * tokens_per_rank */
   void*    eplb_global_stats; /* device [ep_size, eplb_stats_bytes]: row s holds rank s's
                                  eplb_local_stats; NULL when none were passed */
+  int32_t  dispatch_order;  /* order the kernel ran in: MOE_EP_ORDER_SOURCE_ROW or
+                               MOE_EP_ORDER_DESTINATION (AUTO resolved), same for every rank */
 } moe_ep_dispatch_result;
 
 /* Inputs of one combine (MoEEpCommunication, combine()). */

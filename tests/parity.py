@@ -74,12 +74,13 @@ def oracle_params(c: Case) -> oracle.Params:
                          c.eplb_bytes)
 
 
-def make_gpu(c: Case, device="cuda", checkpointable=False):
+def make_gpu(c: Case, device="cuda", checkpointable=False, order="auto"):
     from combine_token_dest_amd import MoEEp
     return MoEEp(c.ep, c.E, c.K, c.cap, c.hidden_size, hidden_row_bytes=c.H, scale_row_bytes=c.S,
                  combine_max_elem_bytes=4 if c.combine_dtype == "f32" else 2,
                  invalid_expert_id=c.invalid_id, enable_rank_mask=c.enable_rank_mask,
-                 eplb_stats_bytes=c.eplb_bytes, checkpointable=checkpointable, device=device)
+                 eplb_stats_bytes=c.eplb_bytes, checkpointable=checkpointable, dispatch_order=order,
+                 device=device)
 
 
 def to_dev(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -173,7 +174,7 @@ def compare_combine(c: Case, gout, oout, tag=""):
             np.testing.assert_array_equal(g, o, err_msg=f"{tag} rank {s}: bfloat16 bits")
 
 
-def run_step(c: Case, *, zero_copy=True, device="cuda", check=True, moe=None):
+def run_step(c: Case, *, zero_copy=True, device="cuda", check=True, moe=None, order="auto"):
     """One dispatch + combine on the GPU and in the oracle; compare both."""
     p = oracle_params(c)
     om = oracle.OracleMoEEp(p)
@@ -184,7 +185,7 @@ def run_step(c: Case, *, zero_copy=True, device="cuda", check=True, moe=None):
 
     own = moe is None
     if own:
-        moe = make_gpu(c, device)
+        moe = make_gpu(c, device, order=order)
     hid, ids, w, sc = upload(c, device)
     mask_arg = None if c.mask is None else c.mask
     gres = moe.dispatch(hid, ids, w, hidden_states_scale=sc, runtime_max_tokens_per_rank=c.rtpr,

@@ -110,7 +110,7 @@ def test_workspace_bytes_cover_the_regions(lib, w):
 @pytest.mark.parametrize("bad", [
     dict(ep_size=0), dict(ep_size=65), dict(num_experts=6, ep_size=4), dict(num_experts=2, ep_size=4),
     dict(top_k=0), dict(max_tokens_per_rank=-1), dict(hidden_size=0), dict(combine_max_elem_bytes=3),
-    dict(hidden_row_bytes=0), dict(scale_row_bytes=-4),
+    dict(hidden_row_bytes=0), dict(scale_row_bytes=-4), dict(dispatch_order=3), dict(dispatch_order=-1),
 ])
 def test_bad_params_rejected(lib, bad):
     assert status_of(_lib.moe_ep_workspace_bytes, params(**bad)) == _lib.MOE_EP_ERR_INVALID_ARG

@@ -34,12 +34,16 @@ def _gpu_ready():
 # --------------------------------------------------------------------------
 # The five workloads at full size
 # --------------------------------------------------------------------------
+ORDERS = ["source", "destination"]
+
+
+@pytest.mark.parametrize("order", ORDERS)
 @pytest.mark.parametrize("name", [w.name for w in wl.WORKLOADS])
-def test_workload_full_size(name):
+def test_workload_full_size(name, order):
     w = wl.BY_NAME[name]
-    log(f"[parity] workload {name} seed {w.seed}")
+    log(f"[parity] workload {name} seed {w.seed} order {order}")
     c = parity.case_from_workload(w)
-    parity.run_step(c, zero_copy=True)
+    parity.run_step(c, zero_copy=True, order=order)
 
 
 def test_dsv3_with_expert_load_statistics():
@@ -61,14 +65,15 @@ def test_workload_separate_combine_input(name):
     parity.run_step(c, zero_copy=False)
 
 
-def test_ragged_steps_on_one_handle():
+@pytest.mark.parametrize("order", ORDERS)
+def test_ragged_steps_on_one_handle(order):
     """Steps with different local counts and tokens_per_rank reuse one handle."""
     w = wl.BY_NAME["ragged"]
     c0 = parity.case_from_workload(w)
-    moe = parity.make_gpu(c0)
+    moe = parity.make_gpu(c0, order=order)
     for i, nt in enumerate([[5, 0, 300, 512, 0, 1, 17, 64], [0] * 8, [1, 0, 0, 0, 0, 0, 0, 0],
                             [512] * 8, [3, 0, 2, 9, 0, 0, 4, 1]]):
-        log(f"[parity] ragged step {i} n={nt}")
+        log(f"[parity] ragged step {i} n={nt} order {order}")
         c = parity.case_from_workload(w, local_num_tokens=nt, seed=2000 + i)
         parity.run_step(c, moe=moe)
     moe.destroy()
@@ -77,16 +82,17 @@ def test_ragged_steps_on_one_handle():
 # --------------------------------------------------------------------------
 # Hand-worked examples through the GPU
 # --------------------------------------------------------------------------
+@pytest.mark.parametrize("order", ORDERS)
 @pytest.mark.parametrize("case", GOLDEN, ids=[g.name for g in GOLDEN])
-def test_golden_on_gpu(case):
-    log(f"[parity] golden {case.name}")
+def test_golden_on_gpu(case, order):
+    log(f"[parity] golden {case.name} order {order}")
     p = case.params
     c = Case(p["ep_size"], p["num_experts"], p["top_k"], p["max_tokens_per_rank"], p["hidden_size"],
              p["hidden_row_bytes"], p["scale_row_bytes"], case.hidden, case.topk_ids, case.topk_weights,
              case.scale, None, case.runtime_max_tokens_per_rank, case.active_rank_mask, case.combine_dtype,
              invalid_id=p["invalid_expert_id"], enable_rank_mask=bool(p["enable_rank_mask"]), name=case.name,
              eplb=case.eplb_local_stats, eplb_bytes=p.get("eplb_stats_bytes", 0))
-    moe = parity.make_gpu(c)
+    moe = parity.make_gpu(c, order=order)
     hid, ids, w, sc = parity.upload(c)
     res = moe.dispatch(hid, ids, w, hidden_states_scale=sc, runtime_max_tokens_per_rank=c.rtpr,
                        active_rank_mask=c.mask, eplb_local_stats=parity.upload_eplb(c))
@@ -174,9 +180,11 @@ EDGE = [
 
 @pytest.mark.parametrize("name,kw", EDGE, ids=[e[0] for e in EDGE])
 def test_edge_case(name, kw):
-    log(f"[parity] edge {name}")
     c = random_case(zlib.crc32(name.encode()) % 10000, name=name, **kw)
-    parity.run_step(c, zero_copy=True)
+    for order in ORDERS:
+        log(f"[parity] edge {name} order {order}")
+        parity.run_step(c, zero_copy=True, order=order)
+    log(f"[parity] edge {name} separate combine input")
     parity.run_step(c, zero_copy=False)
 
 
@@ -241,15 +249,16 @@ def test_expert_output_3d_form():
 # --------------------------------------------------------------------------
 # Writes stay where the method puts them; reads skip what it never needs
 # --------------------------------------------------------------------------
-def test_writes_stay_in_bounds():
+@pytest.mark.parametrize("order", ORDERS)
+def test_writes_stay_in_bounds(order):
     """Workspace bytes the step has no business touching keep a canary, and
     output guard bands stay intact."""
-    log("[parity] canary / guard bands")
+    log(f"[parity] canary / guard bands order {order}")
     c = random_case(11, ep=4, E=8, K=2, cap=16, n=[9, 0, 12, 5], hidden_size=64, H=128, S=20, rtpr=12)
     p = parity.oracle_params(c)
     om = oracle.OracleMoEEp(p)
     ores = om.dispatch(c.hidden, c.ids, c.weights, hidden_states_scale=c.scale, runtime_max_tokens_per_rank=12)
-    moe = parity.make_gpu(c)
+    moe = parity.make_gpu(c, order=order)
     moe.workspace.fill_(0x5A)
     hid, ids, w, sc = parity.upload(c)
     gres = moe.dispatch(hid, ids, w, hidden_states_scale=sc, runtime_max_tokens_per_rank=12)

@@ -129,7 +129,8 @@ bool make_layout(const moe_ep_params* p, Layout* L) {
   const unsigned __int128 parts = (unsigned __int128)L->part_stride * (unsigned __int128)p->ep_size;
   if (parts > limit) return false;
   L->off_route = (int64_t)parts;
-  L->off_counts = L->off_route + align_up((int64_t)(rows * 8), kAlign);
+  L->off_tokens = L->off_route + align_up((int64_t)(rows * 8), kAlign);
+  L->off_counts = L->off_tokens + align_up((int64_t)(rows * sizeof(TokenRec)), kAlign);
   const unsigned __int128 total = (unsigned __int128)L->off_counts + kAlign;
   if (total > limit) return false;
   L->total = (int64_t)total;
@@ -482,6 +483,11 @@ int moe_ep_dispatch(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispa
   }
   k.dev_n = a->local_num_tokens_device;
   k.counts = reinterpret_cast<int32_t*>(h->ws + h->L.off_counts);
+  k.tokens = reinterpret_cast<TokenRec*>(h->ws + h->L.off_tokens);
+  for (int s = 0, start = 0; s < ep; ++s) {
+    k.token_start[s] = start;
+    start += host_n[s];
+  }
   k.off_eplb = h->L.off_eplb;
   k.eplb_bytes = has_e ? p.eplb_stats_bytes : 0;
   k.eplb_vec4 = has_e && (eplb_align_or % 4 == 0);
@@ -597,6 +603,7 @@ int moe_ep_combine(moe_ep_handle h, const moe_ep_combine_args* a, void* stream) 
   k.dev_counts = h->device_counts ? reinterpret_cast<const int32_t*>(h->ws + h->L.off_counts) : nullptr;
   const int vec_elems = (int)(pow2_divisor(align_or, 16) / esz);
   k.route = reinterpret_cast<const uint64_t*>(h->ws + h->L.off_route);
+  k.tokens = reinterpret_cast<const TokenRec*>(h->ws + h->L.off_tokens);
   k.hidden = p.hidden_size;
   k.tpr = h->tpr;
   k.ep = ep;

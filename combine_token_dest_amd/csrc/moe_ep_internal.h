@@ -22,6 +22,7 @@ struct Layout {
   int64_t off_eplb;      // [ep, eplb_stats_bytes]
   int64_t part_stride;   // bytes per rank partition
   int64_t off_route;     // [ep, cap] uint64 destination masks
+  int64_t off_tokens;    // [ep*cap] TokenRec, one per real token in source-rank order (host-count steps)
   int64_t off_counts;    // [ep] int32 token counts of the last dispatch (device-count steps)
   int64_t total;         // workspace bytes
 };
@@ -33,6 +34,14 @@ struct Layout {
 struct OwnerDiv {
   uint64_t magic;
   uint32_t shift;
+};
+
+// What combine needs of real token b (source-rank order): its destination
+// mask and where it sits.  Written by dispatch, read with one 16-byte load.
+struct alignas(16) TokenRec {
+  uint64_t mask;
+  int32_t s;
+  int32_t t;
 };
 
 // Kernel arguments of the dispatch kernel, passed by value.
@@ -63,6 +72,8 @@ struct DispatchKArgs {
   int32_t eplb_vec4;                   // statistics copied as 4-byte words (else bytes)
   const int32_t* dev_n;                // device token counts, or NULL to use n[]
   int32_t* counts;                     // [ep] counts the kernel used (read by combine)
+  TokenRec* tokens;                    // [N] records of the real tokens (host counts only)
+  int32_t token_start[kMaxRanks];      // prefix sums of n[] (host counts only)
   int32_t order;                       // MOE_EP_ORDER_SOURCE_ROW or MOE_EP_ORDER_DESTINATION
   // Destination-major order: rows per block on one XCD, blocks per XCD,
   // column chunks per row, and the number of (destination, row, chunk) items.
@@ -78,7 +89,8 @@ struct CombineKArgs {
   uint8_t* output[kMaxRanks];               // per source rank s: [n_s, hidden]
   int32_t token_start[kMaxRanks + 1];       // prefix sums of n_s (host counts)
   const uint64_t* route;                    // [ep, tpr]
-  const int32_t* dev_counts;                // counts written by dispatch, or NULL to use token_start
+  const TokenRec* tokens;                   // [token_start[ep]] (host-count steps)
+  const int32_t* dev_counts;                // counts written by dispatch, or NULL to use tokens
   int64_t hidden;                           // elements per row
   int32_t tpr;
   int32_t ep;

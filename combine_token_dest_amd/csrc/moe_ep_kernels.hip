@@ -193,7 +193,10 @@ __device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const int r
   const uint64_t m = route_token(a, idr, real);
 
   if (blockIdx.y == 0) {
-    if (threadIdx.x == 0) a.route[r] = m;
+    if (threadIdx.x == 0) {
+      a.route[r] = m;
+      if (real && !a.dev_n) a.tokens[a.token_start[s] + t] = TokenRec{m, s, t};
+    }
     // ids / weights slot of row r on every rank.
     const float* __restrict__ wr = a.has_weights ? a.weights[s] + (int64_t)t * K : nullptr;
     const int slots = a.ep * K;
@@ -379,7 +382,10 @@ __device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const 
   uint8_t* part = a.ws + (int64_t)d * a.part_stride;
 
   if (chunk == 0) {
-    if (d == 0 && threadIdx.x == 0) a.route[r] = m;
+    if (d == 0 && threadIdx.x == 0) {
+      a.route[r] = m;
+      if (real && !a.dev_n) a.tokens[a.token_start[s] + t] = TokenRec{m, s, t};
+    }
     // this destination's ids / weights slot of row r
     for (int jj = threadIdx.x; jj < K; jj += blockDim.x) {
       const int64_t slot = (int64_t)r * K + jj;
@@ -478,26 +484,27 @@ __device__ __forceinline__ typename CVec<DT, VE>::type pack(const float (&acc)[V
   return v;
 }
 
-template <int DT, int VE, int U, int DB, int LP, int SP>
+template <int DT, int VE, int U, int DB, int LP, int SP, bool ONEPASS>
 __device__ __forceinline__ void combine_token(const CombineKArgs& a, const int b) {
   typedef typename CVec<DT, VE>::type V;
-  int s = 0;
+  int s;
   int t;
+  uint64_t m;
   if (a.dev_counts) {
     // Slots of every possible token; those past the count dispatch used hold none.
     s = b / a.tpr;
     t = b - s * a.tpr;
     if (t >= a.dev_counts[s]) return;
+    m = a.route[(int64_t)s * a.tpr + t];
   } else {
-    // Source rank of token b: the last s with token_start[s] <= b (binary
-    // search over the prefix, ep <= 64; empty ranks repeat a start value and
-    // are skipped because the last such s is taken).
-    for (int step = 32; step > 0; step >>= 1)
-      if (s + step < a.ep && b >= a.token_start[s + step]) s += step;
-    t = b - a.token_start[s];
+    // Real token b's record, written by dispatch: one load instead of a
+    // search over the per-source prefix followed by the mask load.
+    const u32x4 rec = *reinterpret_cast<const u32x4*>(a.tokens + b);    // {mask lo, mask hi, s, t}
+    m = ((uint64_t)rec.y << 32) | rec.x;
+    s = (int)rec.z;
+    t = (int)rec.w;
   }
   const int64_t r = (int64_t)s * a.tpr + t;
-  const uint64_t m = a.route[r];
   const int64_t nv = a.hidden / VE;
   constexpr int esz = DT == MOE_EP_F32 ? 4 : 2;
   const int64_t row_bytes = a.hidden * esz;
@@ -553,18 +560,20 @@ __device__ __forceinline__ void combine_token(const CombineKArgs& a, const int b
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (live[u]) buf_store<VB, SP>(out, off[u], pack<DT, VE>(acc[u]));
+    // The grid covers the row: no loop (its back edge measured ~2% slower).
+    if (ONEPASS) break;
   }
 }
 
 // Grid: x = real token (prefix over source ranks), or one of all ep*tpr
 // token slots after a dispatch that read device-resident counts; y = column
 // chunk of the row.
-template <int DT, int VE, int U, int DB, int LP, int SP>
+template <int DT, int VE, int U, int DB, int LP, int SP, bool ONEPASS>
 __global__ void __launch_bounds__(kMaxCombineBlock)
 combine_kernel(const CombineKArgs a) {
   // One workgroup per token slot, no grid-stride loop: with stores ahead of
-  // it in the same workgroup the route-mask load could not be a scalar load.
-  combine_token<DT, VE, U, DB, LP, SP>(a, blockIdx.x);
+  // it in the same workgroup the token-record load could not be a scalar load.
+  combine_token<DT, VE, U, DB, LP, SP, ONEPASS>(a, blockIdx.x);
 }
 
 int round_block(int64_t threads, int max_block) {
@@ -700,8 +709,10 @@ hipError_t launch_combine(const CombineKArgs& a, int dtype, int vec_elems, hipSt
   const LaunchShape sh = combine_shape(a.dev_counts ? (int64_t)a.ep * a.tpr : a.token_start[a.ep], a.hidden, vec_elems);
   if (sh.grid_x <= 0) return hipSuccess;
   const void* fn = nullptr;
+  const bool onepass = (int64_t)sh.grid_y * sh.block * kCombineU >= a.hidden / vec_elems;
 #define MOE_EP_C(DT, VE) \
-    case VE: fn = reinterpret_cast<const void*>(&combine_kernel<DT, VE, kCombineU, kCombineDB, kCombineLP, kCombineSP>); break;
+    case VE: fn = onepass ? reinterpret_cast<const void*>(&combine_kernel<DT, VE, kCombineU, kCombineDB, kCombineLP, kCombineSP, true>) \
+                          : reinterpret_cast<const void*>(&combine_kernel<DT, VE, kCombineU, kCombineDB, kCombineLP, kCombineSP, false>); break;
   if (dtype == MOE_EP_F32) {
     switch (vec_elems) {
       MOE_EP_C(MOE_EP_F32, 4) MOE_EP_C(MOE_EP_F32, 2) MOE_EP_C(MOE_EP_F32, 1)

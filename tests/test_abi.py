@@ -101,8 +101,8 @@ def test_workspace_bytes_cover_the_regions(lib, w):
     rows = w.ep_size * w.max_tokens_per_rank
     per_rank = rows * (w.hidden_row_bytes + w.scale_row_bytes + 8 * w.top_k
                        + w.hidden_size * w.combine_elem_bytes)
-    assert n >= w.ep_size * per_rank + rows * 8
-    assert n <= w.ep_size * (per_rank + 6 * 4096) + rows * 8 + 4096
+    assert n >= w.ep_size * per_rank + rows * (8 + 16)
+    assert n <= w.ep_size * (per_rank + 6 * 4096) + rows * (8 + 16) + 3 * 4096
     if w.name == "large":
         assert n > 2 ** 32           # 64-bit offsets are exercised
 

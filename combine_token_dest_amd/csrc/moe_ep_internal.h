@@ -81,6 +81,8 @@ struct DispatchKArgs {
   int32_t dm_blocks;
   int32_t dm_chunks;
   int64_t dm_items;
+  int32_t dm_u;                        // vectors per thread (7 or 8) and threads per workgroup
+  int32_t dm_threads;
 };
 
 // Kernel arguments of the combine kernel, passed by value.
@@ -100,6 +102,7 @@ struct LaunchShape {
   int grid_x;   // rows (dispatch) or real tokens (combine)
   int grid_y;   // column chunks of a row
   int block;    // threads per workgroup
+  int u;        // vectors per thread
 };
 
 // Fills a.order and the destination-major fields for a step: `requested` is

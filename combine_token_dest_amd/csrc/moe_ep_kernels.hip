@@ -603,7 +603,6 @@ int round_block(int64_t threads, int max_block) {
 //  Capping the grid below one workgroup per row (persistent loops) was
 //  slower for both kernels, and a grid-stride loop alone cost combine 15%
 //  (its route-mask load became a vector load).
-constexpr int kDispatchU = 8;
 constexpr int kDispatchBlock = 128;
 constexpr int kDispatchLP = kCpNt;
 constexpr int kDispatchSP = kCpNt;
@@ -613,12 +612,29 @@ constexpr int kCombineBlock = 1024;
 constexpr int kCombineLP = kCpNt;
 constexpr int kCombineSP = kCpNt;
 
+// Tile of a dispatch workgroup over a row of nv vectors: 8 or 7 vectors per
+// thread and up to kDispatchBlock threads, whichever leaves fewer idle lanes
+// in the row's last chunk (8 on a tie).  A 14 KiB row is 896 16-byte
+// vectors, 128 x 7 exactly; 128 x 8 left 1/8 of the lanes idle and measured
+// ~2% slower.
+LaunchShape row_tile(int64_t rows, int64_t nv) {
+  LaunchShape best{(int)rows, 0, 0, 0};
+  int64_t best_waste = -1;
+  for (int u = 8; u >= 7; --u) {
+    const int block = round_block(std::min<int64_t>(kDispatchBlock, (nv + u - 1) / u), kMaxBlock);
+    const int64_t per = (int64_t)block * u;
+    const int64_t chunks = std::max<int64_t>(1, (nv + per - 1) / per);
+    const int64_t waste = chunks * per - nv;
+    if (best_waste < 0 || waste < best_waste) {
+      best_waste = waste;
+      best = LaunchShape{(int)rows, (int)std::min<int64_t>(kMaxGridY, chunks), block, u};
+    }
+  }
+  return best;
+}
+
 LaunchShape dispatch_shape(int64_t rows, int64_t hidden_bytes, int vec_bytes) {
-  const int64_t nv = hidden_bytes / vec_bytes;
-  const int block = round_block(std::min<int64_t>(kDispatchBlock, (nv + kDispatchU - 1) / kDispatchU), kMaxBlock);
-  const int64_t per_block = (int64_t)block * kDispatchU;
-  const int64_t chunks = std::min<int64_t>(kMaxGridY, std::max<int64_t>(1, (nv + per_block - 1) / per_block));
-  return LaunchShape{(int)rows, (int)chunks, block};
+  return row_tile(rows, hidden_bytes / vec_bytes);
 }
 
 LaunchShape combine_shape(int64_t tokens, int64_t hidden, int vec_elems) {
@@ -626,7 +642,7 @@ LaunchShape combine_shape(int64_t tokens, int64_t hidden, int vec_elems) {
   const int block = round_block(std::min<int64_t>(kCombineBlock, (nv + kCombineU - 1) / kCombineU), kMaxCombineBlock);
   const int64_t per_block = (int64_t)block * kCombineU;
   const int64_t chunks = std::min<int64_t>(kMaxGridY, std::max<int64_t>(1, (nv + per_block - 1) / per_block));
-  return LaunchShape{(int)tokens, (int)chunks, block};
+  return LaunchShape{(int)tokens, (int)chunks, block, kCombineU};
 }
 
 // Destination-major order: rows per XCD block such that a block's source
@@ -636,8 +652,6 @@ LaunchShape combine_shape(int64_t tokens, int64_t hidden, int vec_elems) {
 // 16 or 32 ranks, or 512-token ragged steps, destination-major was 1.7-2x
 // slower (one workgroup per (row, destination), most with nothing to copy).
 constexpr int64_t kDmBlockBytes = 512 * 1024;
-constexpr int kDmU = 8;
-constexpr int kDmBlock = 128;
 constexpr bool kDmSpeculate = false;
 constexpr int64_t kDmAutoMaxPairs = 16384;   // ep * ep * tpr
 constexpr int kDmAutoMaxRanks = 16;
@@ -655,9 +669,9 @@ bool plan_dispatch(DispatchKArgs& a, int vec_bytes, int requested) {
   int64_t b = kDmBlockBytes / std::max<int64_t>(1, a.hidden_bytes);
   b = std::max<int64_t>(1, std::min<int64_t>(b, std::max<int64_t>(1, rmax)));
   const int64_t nq = rmax > 0 ? (rmax + b - 1) / b : 0;
+  const LaunchShape tile = row_tile(0, a.hidden_bytes / vec_bytes);
   const int64_t nv = a.hidden_bytes / vec_bytes;
-  const int64_t per = (int64_t)kDmBlock * kDmU;
-  const int64_t chunks = std::max<int64_t>(1, (nv + per - 1) / per);
+  const int64_t chunks = std::max<int64_t>(1, (nv + (int64_t)tile.block * tile.u - 1) / ((int64_t)tile.block * tile.u));
   // the product is formed in double first: in int64 it can overflow
   const double est = 8.0 * (double)nq * a.ep * (double)b * (double)chunks;
   const int64_t items = est + a.ep > 2147483647.0 ? 0 : 8 * nq * a.ep * b * chunks;
@@ -670,6 +684,8 @@ bool plan_dispatch(DispatchKArgs& a, int vec_bytes, int requested) {
   a.dm_blocks = (int32_t)nq;
   a.dm_chunks = (int32_t)chunks;
   a.dm_items = items;
+  a.dm_u = tile.u;
+  a.dm_threads = tile.block;
   return true;
 }
 
@@ -679,21 +695,25 @@ hipError_t launch_dispatch(const DispatchKArgs& a, int vec_bytes, hipStream_t st
   dim3 grid, block;
   if (a.order == MOE_EP_ORDER_DESTINATION) {
     if (a.dm_items + extra <= 0) return hipSuccess;
+    const bool u8 = a.dm_u == 8;
     switch (vec_bytes) {
 #define MOE_EP_DD(VB) \
-      case VB: fn = reinterpret_cast<const void*>(&dispatch_dst_kernel<VB, kDmU, kDispatchSP, kDmSpeculate>); break;
+      case VB: fn = u8 ? reinterpret_cast<const void*>(&dispatch_dst_kernel<VB, 8, kDispatchSP, kDmSpeculate>) \
+                       : reinterpret_cast<const void*>(&dispatch_dst_kernel<VB, 7, kDispatchSP, kDmSpeculate>); break;
       MOE_EP_DD(16) MOE_EP_DD(8) MOE_EP_DD(4) MOE_EP_DD(2) MOE_EP_DD(1)
 #undef MOE_EP_DD
       default: return hipErrorInvalidValue;
     }
     grid = dim3((unsigned)(a.dm_items + extra));
-    block = dim3(kDmBlock);
+    block = dim3(a.dm_threads);
   } else {
     const LaunchShape sh = dispatch_shape((int64_t)a.ep * a.tpr + extra, a.hidden_bytes, vec_bytes);
     if (sh.grid_x <= 0) return hipSuccess;
+    const bool u8 = sh.u == 8;
     switch (vec_bytes) {
 #define MOE_EP_D(VB) \
-      case VB: fn = reinterpret_cast<const void*>(&dispatch_kernel<VB, kDispatchU, kDispatchLP, kDispatchSP>); break;
+      case VB: fn = u8 ? reinterpret_cast<const void*>(&dispatch_kernel<VB, 8, kDispatchLP, kDispatchSP>) \
+                       : reinterpret_cast<const void*>(&dispatch_kernel<VB, 7, kDispatchLP, kDispatchSP>); break;
       MOE_EP_D(16) MOE_EP_D(8) MOE_EP_D(4) MOE_EP_D(2) MOE_EP_D(1)
 #undef MOE_EP_D
       default: return hipErrorInvalidValue;

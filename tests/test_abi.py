@@ -235,3 +235,19 @@ def test_status_strings(lib):
 
 def test_platform_query_does_not_crash(lib):
     assert _lib.moe_ep_is_platform_supported() in (True, False)
+
+
+def test_destination_order_grid_limit(lib):
+    """An explicit destination-major request whose grid would pass 2^31 - 1
+    workgroups fails before anything is enqueued (64 ranks x 2^19 tokens of
+    16-byte rows: 2^31 items), and leaves the handle idle."""
+    p = params(ep_size=64, num_experts=64, top_k=1, max_tokens_per_rank=1 << 19, hidden_size=8,
+               combine_max_elem_bytes=2, hidden_row_bytes=16, dispatch_order=_lib.MOE_EP_ORDER_DESTINATION)
+    h = _lib.moe_ep_create(p, FAKE_WS, _lib.moe_ep_workspace_bytes(p))
+    a = dispatch_args([0] * 64, rtpr=1 << 19)
+    assert status_of(_lib.moe_ep_dispatch, h, a, 64, 0) == _lib.MOE_EP_ERR_INVALID_ARG
+    assert "grid" in _lib.moe_ep_last_error()
+    ca = _lib.moe_ep_combine_args()
+    ca.active_rank_mask = _lib.MOE_EP_ALL_RANKS
+    assert status_of(_lib.moe_ep_combine, h, ca, 0) == _lib.MOE_EP_ERR_STATE
+    _lib.moe_ep_destroy(h)

@@ -46,6 +46,20 @@ def test_workload_full_size(name, order):
     parity.run_step(c, zero_copy=True, order=order)
 
 
+@pytest.mark.parametrize("name,expect", [("tiny", "destination"), ("dsv3", "destination"),
+                                         ("fp8", "source"), ("ragged", "source")])
+def test_auto_order_choice(name, expect):
+    """AUTO takes the destination-major kernel for decode-sized groups only
+    (ep <= 16 and ep^2 * tokens_per_rank <= 16384), and stays bit-exact."""
+    w = wl.BY_NAME[name]
+    log(f"[parity] workload {name} auto order")
+    c = parity.case_from_workload(w)
+    moe = parity.make_gpu(c)
+    parity.run_step(c, moe=moe)
+    assert moe.last_dispatch_order == expect
+    moe.destroy()
+
+
 def test_dsv3_with_expert_load_statistics():
     """The DeepSeek-V3-shaped round with int32 [256] per-rank statistics gathered."""
     w = wl.BY_NAME["dsv3"]

@@ -311,7 +311,7 @@ dispatch_kernel(const DispatchKArgs a) {
 // others from that XCD's L2 (cached loads), while each destination's rows
 // are written as one sequential sweep (nontemporal stores).
 // ---------------------------------------------------------------------------
-template <int VB, int U, int SP, bool SPEC>
+template <int VB, int U, int SP>
 __device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const int i) {
   typedef typename Bytes<VB>::type V;
   // 32-bit decode: the host keeps the item count below 2^31.
@@ -354,10 +354,6 @@ __device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const 
       v[u] = buf_load<VB, kCpDefault>(src, off[u]);
     }
   };
-  // SPEC: load a real row before its routing is known (the load is wasted
-  // when this destination turns out not to receive it).
-  if (SPEC && real) load_row();
-
   // Destination mask of the token (as route_token, written out here: this
   // form measured ~3% faster in this kernel).
   uint64_t m = 0;
@@ -405,8 +401,10 @@ __device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const 
       }
     }
   }
+  // The row is loaded after the metadata stores: loading it earlier (even
+  // before the routing is known) measured slower.
   if (!routed) return;
-  if (!SPEC) load_row();
+  load_row();
 
   const __amdgpu_buffer_rsrc_t dst =
       row_rsrc(part + a.off_hidden + (int64_t)r * a.hidden_bytes, a.hidden_bytes);
@@ -417,12 +415,12 @@ __device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const 
 
 // Grid: x = destination-major item, then one statistics row per source rank
 // when statistics are gathered.
-template <int VB, int U, int SP, bool SPEC>
+template <int VB, int U, int SP>
 __global__ void __launch_bounds__(kMaxBlock)
 dispatch_dst_kernel(const DispatchKArgs a) {
   const int i = blockIdx.x;
   if (i < a.dm_items) {
-    dispatch_dst_item<VB, U, SP, SPEC>(a, i);
+    dispatch_dst_item<VB, U, SP>(a, i);
   } else {
     gather_stats_row(a, i - (int)a.dm_items);
   }
@@ -652,7 +650,6 @@ LaunchShape combine_shape(int64_t tokens, int64_t hidden, int vec_elems) {
 // 16 or 32 ranks, or 512-token ragged steps, destination-major was 1.7-2x
 // slower (one workgroup per (row, destination), most with nothing to copy).
 constexpr int64_t kDmBlockBytes = 512 * 1024;
-constexpr bool kDmSpeculate = false;
 constexpr int64_t kDmAutoMaxPairs = 16384;   // ep * ep * tpr
 constexpr int kDmAutoMaxRanks = 16;
 
@@ -698,8 +695,8 @@ hipError_t launch_dispatch(const DispatchKArgs& a, int vec_bytes, hipStream_t st
     const bool u8 = a.dm_u == 8;
     switch (vec_bytes) {
 #define MOE_EP_DD(VB) \
-      case VB: fn = u8 ? reinterpret_cast<const void*>(&dispatch_dst_kernel<VB, 8, kDispatchSP, kDmSpeculate>) \
-                       : reinterpret_cast<const void*>(&dispatch_dst_kernel<VB, 7, kDispatchSP, kDmSpeculate>); break;
+      case VB: fn = u8 ? reinterpret_cast<const void*>(&dispatch_dst_kernel<VB, 8, kDispatchSP>) \
+                       : reinterpret_cast<const void*>(&dispatch_dst_kernel<VB, 7, kDispatchSP>); break;
       MOE_EP_DD(16) MOE_EP_DD(8) MOE_EP_DD(4) MOE_EP_DD(2) MOE_EP_DD(1)
 #undef MOE_EP_DD
       default: return hipErrorInvalidValue;

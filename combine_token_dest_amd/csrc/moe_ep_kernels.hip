@@ -4,24 +4,28 @@
 // input region are partition d of one workspace.  Both operations are pure
 // data movement (plus one float32 add per element and routed row in
 // combine), so they are bound by HBM bandwidth; the kernels aim at 16-byte
-// coalesced accesses, every input byte read once, and no workspace traffic
-// beyond what the method moves.
+// coalesced accesses, every input byte read once from HBM, and no workspace
+// traffic beyond what the method moves.
 //
-// dispatch: one workgroup per receive row index r = s*tpr + t.  It works out
-//   the token's destination ranks from its top_k expert ids (contiguous
-//   ownership, masked by the active ranks), writes the top_k ids/weights slot
-//   of row r on every rank (the token's own where routed, invalid_expert_id /
-//   0.0 elsewhere), loads the token's hidden row once into registers and
-//   stores it to every destination, then the scale row the same way.
+// dispatch works out each token's destination ranks from its top_k expert
+//   ids (contiguous ownership, masked by the active ranks), writes the top_k
+//   ids/weights slot of its receive row r = s*tpr + t on every rank (the
+//   token's own where routed, invalid_expert_id / 0.0 elsewhere) and copies
+//   its hidden and scale rows to every destination.  Two kernels do this in
+//   different orders (same bytes): dispatch_kernel, one workgroup per row r
+//   that loads the row once and stores it to each destination in turn, and
+//   dispatch_dst_kernel, one workgroup per (destination, row) with rows
+//   pinned to XCDs so re-reads hit L2.  Both also write, for each real token,
+//   the record combine starts from (mask and position).
 //   Placement and invalid rows: flashinfer.moe_ep.NVLinkOneSidedAlltoAll,
 //   class description; routing: flashinfer.moe_ep.MoEEpCommunication,
 //   dispatch(); mask: NVLinkOneSidedAlltoAll, dispatch().
 //
 // combine: one workgroup per real token (s, t < n_s).  It reads the token's
-//   destination mask and, for each 16-byte column chunk, loads the token's
-//   row from every destination rank (ascending), adds them in float32 in
-//   that order starting from +0.0, rounds once and stores the output row.
-//   Rows of ranks the token did not reach are never read.
+//   record and, for each 16-byte column chunk, loads the token's row from
+//   every destination rank (ascending), adds them in float32 in that order
+//   starting from +0.0, rounds once and stores the output row.  Rows of
+//   ranks the token did not reach are never read.
 //   flashinfer.moe_ep.MoEEpCommunication, combine().
 
 #include <hip/hip_runtime.h>
@@ -105,9 +109,10 @@ __device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, int off, con
 // ---------------------------------------------------------------------------
 // dispatch
 //
-// One receive row r = s*tpr + t per call.  Every workgroup works out the
-// row's destination mask (K scalar loads); chunk 0 (blockIdx.y == 0) also
-// writes the route mask, the ids/weights slot of row r on every rank and the
+// Source-row order: one receive row r = s*tpr + t per workgroup (and
+// column chunk).  Every workgroup works out the row's destination mask (one
+// id load per lane); chunk 0 (blockIdx.y == 0) also writes the route mask,
+// the token record, the ids/weights slot of row r on every rank and the
 // scale row.  Each thread holds U vectors of VB bytes of its column chunk.
 // ---------------------------------------------------------------------------
 // Destination mask of token (s, t): lane j of every wave loads id j, the

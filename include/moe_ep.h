@@ -166,8 +166,9 @@ typedef struct moe_ep_handle_s* moe_ep_handle;
 MOE_EP_API int moe_ep_is_platform_supported(void);
 
 /* Bytes of device workspace a group with these params needs (receive
- * regions, combine input regions and the per-token destination masks, for
- * capacity-sized steps).  *out_bytes is set on success. */
+ * regions, combine input regions, and the per-token destination masks and
+ * records that dispatch leaves for combine, for capacity-sized steps).
+ * *out_bytes is set on success. */
 MOE_EP_API int moe_ep_workspace_bytes(const moe_ep_params* params, size_t* out_bytes);
 
 /* Creates a handle over a caller-owned device workspace of at least

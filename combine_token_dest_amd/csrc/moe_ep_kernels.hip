@@ -159,19 +159,26 @@ __device__ __forceinline__ void write_slot(const DispatchKArgs& a, uint8_t* part
   }
 }
 
-template <int VB, int U, int LP, int SP>
+// Token count of source rank s for this step.  DEVN: read from device memory
+// when the kernel runs (clamped to the rows the buffers hold) and recorded
+// for combine; else the host's count.  The two are separate instantiations:
+// the run-time test alone cost ~2% on the DeepSeek-V3-shaped dispatch.
+template <bool DEVN>
+__device__ __forceinline__ int step_count(const DispatchKArgs& a, const int s, const bool first) {
+  if (!DEVN) return a.n[s];
+  const int c = a.dev_n[s];
+  const int ns = c < 0 ? 0 : (c > a.tpr ? a.tpr : c);
+  if (first && threadIdx.x == 0) a.counts[s] = ns;
+  return ns;
+}
+
+template <int VB, int U, int LP, int SP, bool DEVN>
 __device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const int r) {
   typedef typename Bytes<VB>::type V;
   const int s = r / a.tpr;
   const int t = r - s * a.tpr;
   const int K = a.top_k;
-  int ns = a.n[s];
-  if (a.dev_n) {
-    // Device-resident count, clamped to the rows the buffers hold.
-    const int c = a.dev_n[s];
-    ns = c < 0 ? 0 : (c > a.tpr ? a.tpr : c);
-  }
-  if (t == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.counts[s] = ns;
+  const int ns = step_count<DEVN>(a, s, t == 0 && blockIdx.y == 0);
   const bool real = t < ns;
   const int32_t* __restrict__ idr = a.ids[s] + (int64_t)t * K;
   const int64_t nv = a.hidden_bytes / VB;
@@ -200,7 +207,7 @@ __device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const int r
   if (blockIdx.y == 0) {
     if (threadIdx.x == 0) {
       a.route[r] = m;
-      if (real && !a.dev_n) a.tokens[a.token_start[s] + t] = TokenRec{m, s, t};
+      if (!DEVN && real) a.tokens[a.token_start[s] + t] = TokenRec{m, s, t};
     }
     // ids / weights slot of row r on every rank.
     const float* __restrict__ wr = a.has_weights ? a.weights[s] + (int64_t)t * K : nullptr;
@@ -289,7 +296,7 @@ __device__ __forceinline__ void gather_stats_row(const DispatchKArgs& a, const i
 
 // Grid: x = receive row r = s*tpr + t, then one statistics row per source
 // rank when statistics are gathered; y = column chunk of the hidden row.
-template <int VB, int U, int LP, int SP>
+template <int VB, int U, int LP, int SP, bool DEVN>
 __global__ void __launch_bounds__(kMaxBlock)
 dispatch_kernel(const DispatchKArgs a) {
   // One workgroup per item (no grid-stride loop: a store of one item could
@@ -298,7 +305,7 @@ dispatch_kernel(const DispatchKArgs a) {
   const int rows = a.ep * a.tpr;
   const int r = blockIdx.x;
   if (r < rows) {
-    dispatch_row<VB, U, LP, SP>(a, r);
+    dispatch_row<VB, U, LP, SP, DEVN>(a, r);
   } else if (blockIdx.y == 0) {
     gather_stats_row(a, r - rows);
   }
@@ -316,7 +323,7 @@ dispatch_kernel(const DispatchKArgs a) {
 // others from that XCD's L2 (cached loads), while each destination's rows
 // are written as one sequential sweep (nontemporal stores).
 // ---------------------------------------------------------------------------
-template <int VB, int U, int SP>
+template <int VB, int U, int SP, bool DEVN>
 __device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const int i) {
   typedef typename Bytes<VB>::type V;
   // 32-bit decode: the host keeps the item count below 2^31.
@@ -334,12 +341,7 @@ __device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const 
   const int s = r / a.tpr;
   const int t = r - s * a.tpr;
   const int K = a.top_k;
-  int ns = a.n[s];
-  if (a.dev_n) {
-    const int c = a.dev_n[s];
-    ns = c < 0 ? 0 : (c > a.tpr ? a.tpr : c);
-  }
-  if (t == 0 && d == 0 && chunk == 0 && threadIdx.x == 0) a.counts[s] = ns;
+  const int ns = step_count<DEVN>(a, s, t == 0 && d == 0 && chunk == 0);
   const bool real = t < ns;
   const int32_t* __restrict__ idr = a.ids[s] + (int64_t)t * K;
 
@@ -385,7 +387,7 @@ __device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const 
   if (chunk == 0) {
     if (d == 0 && threadIdx.x == 0) {
       a.route[r] = m;
-      if (real && !a.dev_n) a.tokens[a.token_start[s] + t] = TokenRec{m, s, t};
+      if (!DEVN && real) a.tokens[a.token_start[s] + t] = TokenRec{m, s, t};
     }
     // this destination's ids / weights slot of row r
     for (int jj = threadIdx.x; jj < K; jj += blockDim.x) {
@@ -420,12 +422,12 @@ __device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const 
 
 // Grid: x = destination-major item, then one statistics row per source rank
 // when statistics are gathered.
-template <int VB, int U, int SP>
+template <int VB, int U, int SP, bool DEVN>
 __global__ void __launch_bounds__(kMaxBlock)
 dispatch_dst_kernel(const DispatchKArgs a) {
   const int i = blockIdx.x;
   if (i < a.dm_items) {
-    dispatch_dst_item<VB, U, SP>(a, i);
+    dispatch_dst_item<VB, U, SP, DEVN>(a, i);
   } else {
     gather_stats_row(a, i - (int)a.dm_items);
   }
@@ -691,38 +693,46 @@ bool plan_dispatch(DispatchKArgs& a, int vec_bytes, int requested) {
   return true;
 }
 
+// Kernel for a vector width, a tile width (7 or 8 vectors per thread) and a
+// count source, as a table: (VB, U, DEVN) are template arguments.
+template <template <int, int, bool> class K>
+const void* pick_kernel(int vec_bytes, int u, bool devn) {
+#define MOE_EP_PICK(VB) \
+  case VB: \
+    if (u == 8) return devn ? K<VB, 8, true>::fn() : K<VB, 8, false>::fn(); \
+    return devn ? K<VB, 7, true>::fn() : K<VB, 7, false>::fn();
+  switch (vec_bytes) {
+    MOE_EP_PICK(16) MOE_EP_PICK(8) MOE_EP_PICK(4) MOE_EP_PICK(2) MOE_EP_PICK(1)
+    default: return nullptr;
+  }
+#undef MOE_EP_PICK
+}
+
+template <int VB, int U, bool DEVN> struct SourceRowKernel {
+  static const void* fn() { return reinterpret_cast<const void*>(&dispatch_kernel<VB, U, kDispatchLP, kDispatchSP, DEVN>); }
+};
+template <int VB, int U, bool DEVN> struct DestinationKernel {
+  static const void* fn() { return reinterpret_cast<const void*>(&dispatch_dst_kernel<VB, U, kDispatchSP, DEVN>); }
+};
+
 hipError_t launch_dispatch(const DispatchKArgs& a, int vec_bytes, hipStream_t stream) {
   const int64_t extra = a.eplb_bytes ? a.ep : 0;
+  const bool devn = a.dev_n != nullptr;
   const void* fn;
   dim3 grid, block;
   if (a.order == MOE_EP_ORDER_DESTINATION) {
     if (a.dm_items + extra <= 0) return hipSuccess;
-    const bool u8 = a.dm_u == 8;
-    switch (vec_bytes) {
-#define MOE_EP_DD(VB) \
-      case VB: fn = u8 ? reinterpret_cast<const void*>(&dispatch_dst_kernel<VB, 8, kDispatchSP>) \
-                       : reinterpret_cast<const void*>(&dispatch_dst_kernel<VB, 7, kDispatchSP>); break;
-      MOE_EP_DD(16) MOE_EP_DD(8) MOE_EP_DD(4) MOE_EP_DD(2) MOE_EP_DD(1)
-#undef MOE_EP_DD
-      default: return hipErrorInvalidValue;
-    }
+    fn = pick_kernel<DestinationKernel>(vec_bytes, a.dm_u, devn);
     grid = dim3((unsigned)(a.dm_items + extra));
     block = dim3(a.dm_threads);
   } else {
     const LaunchShape sh = dispatch_shape((int64_t)a.ep * a.tpr + extra, a.hidden_bytes, vec_bytes);
     if (sh.grid_x <= 0) return hipSuccess;
-    const bool u8 = sh.u == 8;
-    switch (vec_bytes) {
-#define MOE_EP_D(VB) \
-      case VB: fn = u8 ? reinterpret_cast<const void*>(&dispatch_kernel<VB, 8, kDispatchLP, kDispatchSP>) \
-                       : reinterpret_cast<const void*>(&dispatch_kernel<VB, 7, kDispatchLP, kDispatchSP>); break;
-      MOE_EP_D(16) MOE_EP_D(8) MOE_EP_D(4) MOE_EP_D(2) MOE_EP_D(1)
-#undef MOE_EP_D
-      default: return hipErrorInvalidValue;
-    }
+    fn = pick_kernel<SourceRowKernel>(vec_bytes, sh.u, devn);
     grid = dim3(sh.grid_x, sh.grid_y);
     block = dim3(sh.block);
   }
+  if (!fn) return hipErrorInvalidValue;
   void* args[] = {const_cast<DispatchKArgs*>(&a)};
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }

@@ -291,7 +291,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also time a plain 1 GiB device-to-device copy (for the PMC byte scale)")
+                    help="(default) time a plain 1 GiB device-to-device copy: the PMC byte scale, and the "
+                         "measured copy bandwidth the round is compared with")
+    ap.add_argument("--no-copy-calibration", action="store_true", help="skip the 1 GiB copy")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -401,7 +403,7 @@ def main():
     traffic = read_traffic(w.name, dominant)
 
     copy_info = None
-    if args.copy_calibration:
+    if not args.no_copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=device)
         dst = torch.empty_like(src)
         for _ in range(3):
@@ -444,6 +446,8 @@ def main():
                    "instances_rotated": I, "seed": w.seed, "dispatch_order": insts[0].order},
         "us_per_round": round(ms_step * 1e3, 2),
         "us_per_round_kernels": round(d_us + c_us, 2),
+        "us_per_round_kernels_p10_p50_p90": [round(float(np.percentile(d_ms + c_ms, q)) * 1e3, 2)
+                                             for q in (10, 50, 90)],
         "timing": "kernel times from fence-free HIP events around runs of I back-to-back launches",
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "pct_hbm_peak_kernels": round(100 * bytes_round / ((d_us + c_us) * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
@@ -469,6 +473,7 @@ def main():
     }
     if copy_info:
         out["copy_1GiB"] = copy_info
+        out["pct_of_copy_bw"] = round(100 * value / copy_info["GB/s"], 2)
     print(json.dumps(out), flush=True)
 
 

@@ -328,7 +328,10 @@ def main():
     dev_inputs = (dev_hidden, dev_ids, dev_w, dev_s, dev_vals)
 
     log(f"[bench] building {args.instances} instances")
-    insts = [Instance(w, inp, dev_inputs, device, args.dispatch_order) for _ in range(args.instances)]
+    insts = []
+    for i in range(args.instances):
+        insts.append(Instance(w, inp, dev_inputs, device, args.dispatch_order))
+        log(f"[bench] instance {i + 1}/{args.instances} ready")
     del dev_vals
     torch.cuda.synchronize()
     tpr = insts[0].tpr

@@ -81,15 +81,16 @@ def test_graph_replays_match_oracle(name):
     moe.destroy()
 
 
-def test_graph_replays_ragged_steps_with_device_counts():
+@pytest.mark.parametrize("order", ["source", "destination"])
+def test_graph_replays_ragged_steps_with_device_counts(order):
     """One captured round replays steps whose token counts differ: the counts
     live in device memory and the kernels read them when they run."""
     w = wl.BY_NAME["ragged"]
     cap = w.max_tokens_per_rank
-    log("[graph] capture ragged with device-resident counts")
+    log(f"[graph] capture ragged with device-resident counts, {order} order")
     full = parity.case_from_workload(w, local_num_tokens=[cap] * w.ep_size, seed=500)
     full.rtpr = None
-    moe = parity.make_gpu(full)
+    moe = parity.make_gpu(full, order=order)
     hid, ids, wts, _ = parity.upload(full)
     counts = torch.full((w.ep_size,), cap, dtype=torch.int32, device="cuda")
     rows = w.ep_size * cap
@@ -135,13 +136,14 @@ def test_graph_replays_ragged_steps_with_device_counts():
     moe.destroy()
 
 
-def test_device_counts_are_clamped_to_the_buffers():
+@pytest.mark.parametrize("order", ["source", "destination"])
+def test_device_counts_are_clamped_to_the_buffers(order):
     """Counts outside [0, tokens_per_rank] are clamped by the kernels."""
     w = wl.BY_NAME["tiny"]
     cap = w.max_tokens_per_rank
-    log("[graph] device counts clamped")
+    log(f"[graph] device counts clamped, {order} order")
     full = parity.case_from_workload(w)
-    moe = parity.make_gpu(full)
+    moe = parity.make_gpu(full, order=order)
     hid, ids, wts, _ = parity.upload(full)
     counts = torch.tensor([-3, cap + 100, 5, cap], dtype=torch.int32, device="cuda")
     res = moe.dispatch(hid, ids, wts, local_num_tokens_device=counts)

@@ -177,6 +177,8 @@ EDGE = [
     ("no_weights", dict(ep=4, E=8, K=3, cap=8, n=[8, 1, 0, 5], hidden_size=32, H=64, weights=False)),
     ("big_row_multi_pass", dict(ep=2, E=4, K=2, cap=6, n=[6, 5], hidden_size=40000, H=80000)),
     ("k16", dict(ep=8, E=256, K=16, cap=32, n=[32] * 8, hidden_size=128, H=256)),
+    ("k65_crosses_a_wave", dict(ep=4, E=256, K=65, cap=5, n=[5, 3, 0, 2], hidden_size=64, H=128)),
+    ("k130_crosses_a_workgroup", dict(ep=2, E=512, K=130, cap=3, n=[3, 1], hidden_size=32, H=64)),
     ("wide_ep64", dict(ep=64, E=128, K=8, cap=4, n=[4] * 64, hidden_size=64, H=128,
                        mask=((1 << 64) - 1) & ~(1 << 5))),
     ("ep64_bit63_only", dict(ep=64, E=64, K=4, cap=3, n=[3] * 64, hidden_size=16, H=32, mask=1 << 63)),

@@ -157,10 +157,15 @@ class MoEEp:
         a = _lib.moe_ep_dispatch_args()
         wp = sp = 0
         n = []
+        keep = []              # int32 copies of int64 ids, alive until the call returns
         for s in range(ep):
             h, ids = hidden_states[s], topk_ids[s]
+            if ids.dtype == torch.int64:
+                # The library takes int32 ids; expert ids must fit in int32.
+                ids = ids.to(torch.int32)
+                keep.append(ids)
             if ids.dtype != torch.int32:
-                raise TypeError("topk_ids must be int32")
+                raise TypeError("topk_ids must be int32 (or int64, converted)")
             if ids.dim() != 2 or ids.shape[1] != p.top_k:
                 raise ValueError(f"rank {s}: topk_ids must be [n, {p.top_k}]")
             ns = ids.shape[0]

@@ -242,6 +242,22 @@ def test_misaligned_rows_use_narrow_vectors():
         moe.destroy()
 
 
+def test_int64_topk_ids_are_accepted():
+    """The wrapper converts int64 expert ids to the library's int32."""
+    log("[parity] int64 topk_ids")
+    c = random_case(21, ep=4, E=16, K=4, cap=9, n=[9, 0, 4, 7], hidden_size=64, H=128)
+    p = parity.oracle_params(c)
+    om = oracle.OracleMoEEp(p)
+    ores = om.dispatch(c.hidden, c.ids, c.weights)
+    moe = parity.make_gpu(c)
+    hid, ids, w, _ = parity.upload(c)
+    gres = moe.dispatch(hid, [i.to(torch.int64) for i in ids], w)
+    torch.cuda.synchronize()
+    parity.compare_dispatch(c, gres, ores, "int64 ids")
+    moe.combine([moe.get_combine_input_buffer(d, torch.bfloat16) for d in range(c.ep)])
+    moe.destroy()
+
+
 def test_expert_output_3d_form():
     """[ep, tpr, hidden] is accepted as the same memory as [ep*tpr, hidden]."""
     log("[parity] expert_output as [ep, tpr, hidden]")

@@ -389,7 +389,10 @@ __device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const 
       a.route[r] = m;
       if (!DEVN && real) a.tokens[a.token_start[s] + t] = TokenRec{m, s, t};
     }
-    // this destination's ids / weights slot of row r
+    // This destination's ids / weights slot of row r.  Written as selects
+    // (the compiler turns the id select into one load from either source):
+    // here that measured a few percent faster than write_slot's branches,
+    // which the source-row kernel keeps.
     for (int jj = threadIdx.x; jj < K; jj += blockDim.x) {
       const int64_t slot = (int64_t)r * K + jj;
       reinterpret_cast<int32_t*>(part + a.off_ids)[slot] = routed ? idr[jj] : a.invalid_id;

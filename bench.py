@@ -51,7 +51,7 @@ def log(msg):
 # algorithmic bytes
 # ---------------------------------------------------------------------------
 def algorithmic_bytes(w, n, masks, tpr, has_w):
-    """Bytes the method must move in one round (see the design doc's table):
+    """Bytes the method must move in one round:
     dispatch reads every real token's ids, weights, hidden and scale row once,
     writes every routed (token, rank) pair's hidden and scale row, and writes
     the ids (and weights) slot of every receive row of every rank; combine

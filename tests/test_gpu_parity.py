@@ -204,6 +204,41 @@ def test_edge_case(name, kw):
     parity.run_step(c, zero_copy=False)
 
 
+def random_small_config(seed):
+    """A random small step: any ep up to 16, top_k up to 10, ragged counts
+    (some ranks empty), odd row sizes, optional scales, weights, mask,
+    runtime bound and statistics."""
+    rng = np.random.default_rng(seed)
+    ep = int(rng.integers(1, 17))
+    K = int(rng.integers(1, 11))
+    E = ep * int(rng.integers(1, 9))
+    cap = int(rng.integers(0, 41))
+    n = [int(rng.integers(0, cap + 1)) if rng.random() < 0.8 else 0 for _ in range(ep)]
+    dtype = "f32" if rng.random() < 0.3 else "bf16"
+    hidden_size = int(rng.choice([1, 3, 8, 50, 128, 515, 2048]))
+    H = int(rng.choice([2, 6, 12, 24, 100, 256, 1030, 4104]))
+    S = int(rng.choice([0, 0, 4, 13, 56]))
+    rtpr = None if rng.random() < 0.5 else int(rng.integers(max(n + [0]), cap + 1))
+    mask = None
+    if ep > 1 and rng.random() < 0.4:
+        mask = int(rng.integers(0, 1 << ep))
+    invalid = -1 if rng.random() < 0.7 else E
+    eplb = int(rng.choice([0, 0, 7, 64]))
+    return dict(ep=ep, E=E, K=K, cap=cap, n=n, hidden_size=hidden_size, H=H, S=S, rtpr=rtpr, mask=mask,
+                dtype=dtype, weights=rng.random() < 0.85, invalid=invalid, id_lo=-1, id_hi=E + 1, eplb=eplb)
+
+
+def test_random_small_configs():
+    """40 seeded random steps, both dispatch orders, against the oracle."""
+    for seed in range(40):
+        kw = random_small_config(seed)
+        c = random_case(7000 + seed, name=f"random{seed}", **kw)
+        for order in ORDERS:
+            log(f"[parity] random config {seed} order {order}: ep={kw['ep']} K={kw['K']} "
+                f"n={kw['n']} H={kw['H']} S={kw['S']} {kw['dtype']}")
+            parity.run_step(c, zero_copy=order == "source", order=order)
+
+
 def test_misaligned_rows_use_narrow_vectors():
     """Row pointers offset by 1, 2, 4 and 8 bytes from 16-byte alignment."""
     for off in (1, 2, 4, 8):

@@ -48,6 +48,16 @@ def test_exports_match_header(lib):
     assert exported == set(declared)
 
 
+@pytest.mark.parametrize("compiler,std", [("gcc", "-std=c99"), ("g++", "-std=c++11")])
+def test_header_stands_alone(compiler, std):
+    """include/moe_ep.h compiles on its own as C and as C++, warning-free."""
+    with tempfile.TemporaryDirectory() as tmp:
+        src = os.path.join(tmp, "use.c" if compiler == "gcc" else "use.cpp")
+        open(src, "w").write('#include "moe_ep.h"\nint main(void) { moe_ep_params p; (void)p; return 0; }\n')
+        subprocess.run([compiler, std, "-Wall", "-Wextra", "-Werror", "-pedantic", "-fsyntax-only",
+                        "-I", os.path.join(ROOT, "include"), src], check=True)
+
+
 def test_struct_layouts_match_header(lib):
     """ctypes mirrors of the header structs have C's sizes and offsets."""
     structs = {

@@ -39,7 +39,9 @@ if ROOT not in sys.path:
 
 METRIC = "dispatch+combine µs/round and effective HBM GB/s (% peak), DSv3 shape"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
-KERNEL_SOURCE = os.path.join(ROOT, "combine_token_dest_amd", "csrc", "moe_ep_kernels.hip")
+# The kernels and the host code that picks their launch shapes.
+KERNEL_SOURCES = [os.path.join(ROOT, "combine_token_dest_amd", "csrc", f)
+                  for f in ("moe_ep_kernels.hip", "moe_ep_plan.cpp", "moe_ep_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{workload}.txt")
 
 
@@ -249,11 +251,13 @@ class HipEvents:
 
 
 def kernel_source_hash():
-    """sha256[:16] of the kernel source with comments and whitespace removed,
+    """sha256[:16] of the kernel sources with comments and whitespace removed,
     so the PMC traffic figures stay tied to the code they were taken on."""
     import re
-    with open(KERNEL_SOURCE) as f:
-        src = f.read()
+    src = ""
+    for path in KERNEL_SOURCES:
+        with open(path) as f:
+            src += f.read() + "\n"
     src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
     src = re.sub(r"//[^\n]*", " ", src)
     src = " ".join(src.split())

@@ -42,12 +42,14 @@ def build(verbose: bool = False) -> str:
     with tempfile.TemporaryDirectory(prefix="moe_ep_build_") as tmp:
         k_obj = os.path.join(tmp, "moe_ep_kernels.o")
         a_obj = os.path.join(tmp, "moe_ep_api.o")
+        p_obj = os.path.join(tmp, "moe_ep_plan.o")
         lib_tmp = os.path.join(tmp, LIB_NAME)
         steps = [
             [HIPCC, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, "-x", "hip", "-c",
              os.path.join(CSRC, "moe_ep_kernels.hip"), "-o", k_obj],
             [HIPCC, *COMMON, "-c", os.path.join(CSRC, "moe_ep_api.cpp"), "-o", a_obj],
-            [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", k_obj, a_obj, "-o", lib_tmp],
+            [HIPCC, *COMMON, "-c", os.path.join(CSRC, "moe_ep_plan.cpp"), "-o", p_obj],
+            [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", k_obj, a_obj, p_obj, "-o", lib_tmp],
         ]
         for cmd in steps:
             out = _run(cmd)

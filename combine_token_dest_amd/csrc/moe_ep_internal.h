@@ -98,6 +98,34 @@ struct CombineKArgs {
   int32_t ep;
 };
 
+// Launch configurations, chosen by timing variants on MI355X in the same
+// alternation the bench uses (8 workspaces rotated so the 256 MB MALL holds
+// none of the data between uses; 8 dispatches then 8 combines), mostly with
+// the DeepSeek-V3-shaped round (ep 8, 128 tokens per rank, 14 KiB rows):
+//  - dispatch: up to 128 threads with 7 or 8 vectors of 16 B each, whichever
+//    leaves fewer idle lanes (a 14 KiB row is 128 x 7).  In the source-row
+//    order all waves of a workgroup store a destination row before moving to
+//    the next: interleaving the destinations per vector halved throughput,
+//    and staggered orders, blocked lane maps or several rows per workgroup
+//    were 2-10% slower.  Destination-major workgroups of one wave, 4 waves
+//    or 7 waves were 7-58% slower than 2.
+//  - combine: one column vector per thread, a whole row per workgroup (up to
+//    1024 threads), all (up to 8) destination rows loaded in one batch: 5%
+//    faster than 2 vectors x 4 rows per batch.
+//  - nontemporal loads and stores in both (the cache policies are in the
+//    kernels): cached combine loads were ~40% slower, and sc1 or default
+//    dispatch stores ~45% slower.
+//  Capping the grid below one workgroup per row (persistent loops) was
+//  slower for both kernels, and a grid-stride loop alone cost combine 15%
+//  (its route-mask load became a vector load).
+constexpr int kMaxBlock = 512;           // dispatch workgroups (launch bound)
+constexpr int kMaxCombineBlock = 1024;   // combine workgroups: one whole row (launch bound)
+constexpr int64_t kMaxGridY = 65535;     // chunks beyond this are looped over inside a workgroup
+constexpr int kDispatchBlock = 128;      // dispatch threads per workgroup, at most
+constexpr int kCombineU = 1;             // combine: vectors per thread
+constexpr int kCombineDB = 8;            // combine: destination rows loaded per batch
+constexpr int kCombineBlock = 1024;      // combine threads per workgroup, at most
+
 struct LaunchShape {
   int grid_x;   // rows (dispatch) or real tokens (combine)
   int grid_y;   // column chunks of a row
@@ -118,7 +146,8 @@ hipError_t launch_dispatch(const DispatchKArgs& a, int vec_bytes, hipStream_t st
 // divide the hidden size and every row pointer's alignment in elements.
 hipError_t launch_combine(const CombineKArgs& a, int dtype, int vec_elems, hipStream_t stream);
 
-// Launch shapes the two launchers use (exposed for tests of the host logic).
+// Launch shapes the two launchers use (host code, moe_ep_plan.cpp).
+LaunchShape row_tile(int64_t rows, int64_t nv);
 LaunchShape dispatch_shape(int64_t rows, int64_t hidden_bytes, int vec_bytes);
 LaunchShape combine_shape(int64_t tokens, int64_t hidden, int vec_elems);
 

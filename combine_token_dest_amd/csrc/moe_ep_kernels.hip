@@ -48,9 +48,6 @@ template <> struct Bytes<4> { typedef uint32_t type; };
 template <> struct Bytes<2> { typedef uint16_t type; };
 template <> struct Bytes<1> { typedef uint8_t type; };
 
-constexpr int kMaxBlock = 512;          // dispatch workgroups
-constexpr int kMaxCombineBlock = 1024;  // combine workgroups (one whole row)
-constexpr int64_t kMaxGridY = 65535;   // chunks beyond this are looped over inside a workgroup
 
 __device__ __forceinline__ int expert_owner(const OwnerDiv& od, uint32_t e) {
   return (int)(((uint64_t)e * od.magic) >> od.shift);
@@ -584,117 +581,15 @@ combine_kernel(const CombineKArgs a) {
   combine_token<DT, VE, U, DB, LP, SP, ONEPASS>(a, blockIdx.x);
 }
 
-int round_block(int64_t threads, int max_block) {
-  int64_t b = (threads + 63) / 64 * 64;
-  if (b < 64) b = 64;
-  if (b > max_block) b = max_block;
-  return (int)b;
-}
 
 }  // namespace
 
-// Launch configurations, chosen by timing variants on MI355X in the same
-// alternation the bench uses (8 workspaces rotated so the 256 MB MALL holds
-// none of the data between uses; 8 dispatches then 8 combines) with the
-// DeepSeek-V3-shaped round (ep 8, 128 tokens per rank, 14 KiB rows):
-//  - dispatch: 8 vectors of 16 B per thread and up to 128 threads, so one
-//    workgroup carries up to 16 KiB of a row.  All waves of a workgroup
-//    store a destination row before moving to the next: interleaving the
-//    destinations per vector halved throughput, and staggering the order
-//    across waves, blocked lane mappings, several rows per workgroup or
-//    1-wave workgroups were all 2-10% slower.
-//  - combine: one column vector per thread, a whole row per workgroup (up to
-//    1024 threads), all (up to 8) destination rows loaded in one batch: 5%
-//    faster than 2 vectors x 4 rows per batch.
-//  - nontemporal loads and stores in both: cached combine loads were ~40%
-//    slower, and sc1 (or sc0 sc1) dispatch stores ~8% slower.
-//  Capping the grid below one workgroup per row (persistent loops) was
-//  slower for both kernels, and a grid-stride loop alone cost combine 15%
-//  (its route-mask load became a vector load).
-constexpr int kDispatchBlock = 128;
+// Cache policies of the row accesses (see the tuning notes with the launch
+// constants in moe_ep_internal.h).
 constexpr int kDispatchLP = kCpNt;
 constexpr int kDispatchSP = kCpNt;
-constexpr int kCombineU = 1;
-constexpr int kCombineDB = 8;
-constexpr int kCombineBlock = 1024;
 constexpr int kCombineLP = kCpNt;
 constexpr int kCombineSP = kCpNt;
-
-// Tile of a dispatch workgroup over a row of nv vectors: 8 or 7 vectors per
-// thread and up to kDispatchBlock threads, whichever leaves fewer idle lanes
-// in the row's last chunk (8 on a tie).  A 14 KiB row is 896 16-byte
-// vectors, 128 x 7 exactly; 128 x 8 left 1/8 of the lanes idle and measured
-// ~2% slower.
-LaunchShape row_tile(int64_t rows, int64_t nv) {
-  LaunchShape best{(int)rows, 0, 0, 0};
-  int64_t best_waste = -1;
-  for (int u = 8; u >= 7; --u) {
-    const int block = round_block(std::min<int64_t>(kDispatchBlock, (nv + u - 1) / u), kMaxBlock);
-    const int64_t per = (int64_t)block * u;
-    const int64_t chunks = std::max<int64_t>(1, (nv + per - 1) / per);
-    const int64_t waste = chunks * per - nv;
-    if (best_waste < 0 || waste < best_waste) {
-      best_waste = waste;
-      best = LaunchShape{(int)rows, (int)std::min<int64_t>(kMaxGridY, chunks), block, u};
-    }
-  }
-  return best;
-}
-
-LaunchShape dispatch_shape(int64_t rows, int64_t hidden_bytes, int vec_bytes) {
-  return row_tile(rows, hidden_bytes / vec_bytes);
-}
-
-LaunchShape combine_shape(int64_t tokens, int64_t hidden, int vec_elems) {
-  const int64_t nv = hidden / vec_elems;
-  const int block = round_block(std::min<int64_t>(kCombineBlock, (nv + kCombineU - 1) / kCombineU), kMaxCombineBlock);
-  const int64_t per_block = (int64_t)block * kCombineU;
-  const int64_t chunks = std::min<int64_t>(kMaxGridY, std::max<int64_t>(1, (nv + per_block - 1) / per_block));
-  return LaunchShape{(int)tokens, (int)chunks, block, kCombineU};
-}
-
-// Destination-major order: rows per XCD block such that a block's source
-// rows (about 512 KiB) stay in the XCD's L2 while every destination re-reads
-// them.  AUTO takes it for decode-sized groups, where it was ~7% faster on
-// the DeepSeek-V3-shaped dispatch, and the source-row order elsewhere: with
-// 16 or 32 ranks, or 512-token ragged steps, destination-major was 1.7-2x
-// slower (one workgroup per (row, destination), most with nothing to copy).
-constexpr int64_t kDmBlockBytes = 512 * 1024;
-constexpr int64_t kDmAutoMaxPairs = 16384;   // ep * ep * tpr
-constexpr int kDmAutoMaxRanks = 16;
-
-bool plan_dispatch(DispatchKArgs& a, int vec_bytes, int requested) {
-  const int64_t rows = (int64_t)a.ep * a.tpr;
-  int order = requested;
-  if (order == MOE_EP_ORDER_AUTO)
-    order = (a.ep <= kDmAutoMaxRanks && rows * a.ep <= kDmAutoMaxPairs) ? MOE_EP_ORDER_DESTINATION
-                                                                         : MOE_EP_ORDER_SOURCE_ROW;
-  a.order = order;
-  a.dm_items = 0;
-  if (order != MOE_EP_ORDER_DESTINATION) return true;
-  const int64_t rmax = (rows + 7) / 8;
-  int64_t b = kDmBlockBytes / std::max<int64_t>(1, a.hidden_bytes);
-  b = std::max<int64_t>(1, std::min<int64_t>(b, std::max<int64_t>(1, rmax)));
-  const int64_t nq = rmax > 0 ? (rmax + b - 1) / b : 0;
-  const LaunchShape tile = row_tile(0, a.hidden_bytes / vec_bytes);
-  const int64_t nv = a.hidden_bytes / vec_bytes;
-  const int64_t chunks = std::max<int64_t>(1, (nv + (int64_t)tile.block * tile.u - 1) / ((int64_t)tile.block * tile.u));
-  // the product is formed in double first: in int64 it can overflow
-  const double est = 8.0 * (double)nq * a.ep * (double)b * (double)chunks;
-  const int64_t items = est + a.ep > 2147483647.0 ? 0 : 8 * nq * a.ep * b * chunks;
-  if (est + a.ep > 2147483647.0) {
-    if (requested != MOE_EP_ORDER_AUTO) return false;
-    a.order = MOE_EP_ORDER_SOURCE_ROW;
-    return true;
-  }
-  a.dm_block_rows = (int32_t)b;
-  a.dm_blocks = (int32_t)nq;
-  a.dm_chunks = (int32_t)chunks;
-  a.dm_items = items;
-  a.dm_u = tile.u;
-  a.dm_threads = tile.block;
-  return true;
-}
 
 // Kernel for a vector width, a tile width (7 or 8 vectors per thread) and a
 // count source, as a table: (VB, U, DEVN) are template arguments.

@@ -1,0 +1,144 @@
+// Host-only driver of the C ABI's validation and planning paths, built with
+// the address and undefined-behaviour sanitizers by tests/test_host_sanitized.py.
+// No call here reaches the GPU: every dispatch/combine below is rejected by
+// the host checks before anything is enqueued, so the two kernel launchers
+// are stubs that must never run.
+
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <initializer_list>
+
+#include "moe_ep.h"
+#include "moe_ep_internal.h"
+
+namespace moe_ep_detail {
+hipError_t launch_dispatch(const DispatchKArgs&, int, hipStream_t) {
+  std::printf("launch_dispatch reached\n");
+  return hipErrorInvalidValue;
+}
+hipError_t launch_combine(const CombineKArgs&, int, int, hipStream_t) {
+  std::printf("launch_combine reached\n");
+  return hipErrorInvalidValue;
+}
+}  // namespace moe_ep_detail
+
+namespace {
+
+void* const kFakeWorkspace = reinterpret_cast<void*>(uintptr_t(1) << 40);
+int g_fails = 0;
+
+void expect(bool ok, const char* what) {
+  if (!ok) {
+    std::printf("FAILED: %s (%s)\n", what, moe_ep_last_error());
+    ++g_fails;
+  }
+}
+
+moe_ep_params base() {
+  moe_ep_params p;
+  std::memset(&p, 0, sizeof(p));
+  p.ep_size = 4;
+  p.num_experts = 8;
+  p.top_k = 2;
+  p.max_tokens_per_rank = 16;
+  p.hidden_size = 128;
+  p.combine_max_elem_bytes = 4;
+  p.hidden_row_bytes = 512;
+  p.invalid_expert_id = -1;
+  return p;
+}
+
+}  // namespace
+
+int main() {
+  size_t n = 0;
+  // Sizes at and beyond every limit: the layout arithmetic must not overflow.
+  for (int ep : {-1, 0, 1, 3, 8, 64, 65})
+    for (int cap : {-5, 0, 1, 1 << 20, 1 << 25, 1 << 30})
+      for (long long hb : {1LL, 7LL, 14336LL, (1LL << 31) - 1, 1LL << 31})
+        for (int order : {-1, 0, 1, 2, 3}) {
+          moe_ep_params p = base();
+          p.ep_size = ep;
+          p.num_experts = ep > 0 ? 2 * ep : 2;
+          p.max_tokens_per_rank = cap;
+          p.hidden_row_bytes = hb;
+          p.scale_row_bytes = hb / 3;
+          p.eplb_stats_bytes = hb / 5;
+          p.dispatch_order = order;
+          (void)moe_ep_workspace_bytes(&p, &n);
+        }
+
+  // Launch shapes over many row sizes: every tile covers its row.
+  using moe_ep_detail::LaunchShape;
+  for (int64_t nv = 1; nv <= 70000; nv = nv < 64 ? nv + 1 : nv * 3 / 2) {
+    const LaunchShape t = moe_ep_detail::row_tile(7, nv);
+    expect(t.u == 7 || t.u == 8, "tile u");
+    expect(t.block % 64 == 0 && t.block <= moe_ep_detail::kDispatchBlock, "tile block");
+    expect((int64_t)t.grid_y * t.block * t.u >= nv || t.grid_y == moe_ep_detail::kMaxGridY, "tile covers the row");
+    const LaunchShape c = moe_ep_detail::combine_shape(5, nv, 1);
+    expect((int64_t)c.grid_y * c.block * c.u >= nv || c.grid_y == moe_ep_detail::kMaxGridY, "combine covers the row");
+  }
+
+  // Validation paths of one handle over a fake workspace.
+  moe_ep_params p = base();
+  expect(moe_ep_workspace_bytes(&p, &n) == MOE_EP_OK, "workspace_bytes");
+  moe_ep_handle h = nullptr;
+  expect(moe_ep_create(&p, kFakeWorkspace, n, &h) == MOE_EP_OK, "create");
+  moe_ep_dispatch_args a;
+  std::memset(&a, 0, sizeof(a));
+  a.runtime_max_tokens_per_rank = -1;
+  a.active_rank_mask = MOE_EP_ALL_RANKS;
+  moe_ep_dispatch_result res[MOE_EP_MAX_RANKS];
+  a.local_num_tokens[0] = 17;
+  expect(moe_ep_dispatch(h, &a, res, nullptr) == MOE_EP_ERR_CAPACITY, "capacity");
+  a.local_num_tokens[0] = 5;
+  expect(moe_ep_dispatch(h, &a, res, nullptr) == MOE_EP_ERR_INVALID_ARG, "NULL rows");
+  a.hidden[0] = kFakeWorkspace;
+  a.topk_ids[0] = reinterpret_cast<const int32_t*>(static_cast<char*>(kFakeWorkspace) + 2);
+  expect(moe_ep_dispatch(h, &a, res, nullptr) == MOE_EP_ERR_ALIGN, "misaligned ids");
+  a.topk_ids[0] = static_cast<const int32_t*>(kFakeWorkspace);
+  a.active_rank_mask = 0x3;
+  expect(moe_ep_dispatch(h, &a, res, nullptr) == MOE_EP_ERR_MASK, "mask without enable");
+  a.active_rank_mask = MOE_EP_ALL_RANKS;
+  a.weights_present = 0x1;
+  a.topk_weights[0] = static_cast<const float*>(kFakeWorkspace);
+  expect(moe_ep_dispatch(h, &a, res, nullptr) == MOE_EP_ERR_INVALID_ARG, "weights from some ranks");
+  moe_ep_combine_args c;
+  std::memset(&c, 0, sizeof(c));
+  c.active_rank_mask = MOE_EP_ALL_RANKS;
+  expect(moe_ep_combine(h, &c, nullptr) == MOE_EP_ERR_STATE, "combine before dispatch");
+  void* buf = nullptr;
+  expect(moe_ep_get_combine_input_buffer(h, 0, MOE_EP_F32, &buf) == MOE_EP_ERR_STATE, "buffer before dispatch");
+  expect(moe_ep_checkpoint_prepare(h) == MOE_EP_ERR_UNSUPPORTED, "checkpoint on a caller workspace");
+  expect(moe_ep_destroy(h) == MOE_EP_OK, "destroy");
+  expect(moe_ep_destroy(nullptr) == MOE_EP_OK, "destroy NULL");
+
+  // An explicit destination-major request whose grid passes 2^31 - 1.
+  p = base();
+  p.ep_size = 64;
+  p.num_experts = 64;
+  p.top_k = 1;
+  p.max_tokens_per_rank = 1 << 19;
+  p.hidden_size = 8;
+  p.combine_max_elem_bytes = 2;
+  p.hidden_row_bytes = 16;
+  p.dispatch_order = MOE_EP_ORDER_DESTINATION;
+  expect(moe_ep_workspace_bytes(&p, &n) == MOE_EP_OK, "workspace_bytes 2");
+  expect(moe_ep_create(&p, kFakeWorkspace, n, &h) == MOE_EP_OK, "create 2");
+  std::memset(&a, 0, sizeof(a));
+  a.runtime_max_tokens_per_rank = 1 << 19;
+  a.active_rank_mask = MOE_EP_ALL_RANKS;
+  expect(moe_ep_dispatch(h, &a, res, nullptr) == MOE_EP_ERR_INVALID_ARG, "grid limit");
+  expect(moe_ep_destroy(h) == MOE_EP_OK, "destroy 2");
+
+  int32_t ranks[] = {0, 5, 63};
+  uint64_t m = 0;
+  expect(moe_ep_active_rank_mask(ranks, 3, &m) == MOE_EP_OK && m == ((1ull << 63) | (1ull << 5) | 1ull), "mask helper");
+  int32_t bad[] = {64};
+  expect(moe_ep_active_rank_mask(bad, 1, &m) == MOE_EP_ERR_MASK, "mask helper range");
+  for (int s = -9; s <= 2; ++s) expect(moe_ep_status_string(s) != nullptr, "status string");
+
+  std::printf("fails %d\n", g_fails);
+  return g_fails == 0 ? 0 : 1;
+}

@@ -591,13 +591,14 @@ constexpr int kDispatchSP = kCpNt;
 constexpr int kCombineLP = kCpNt;
 constexpr int kCombineSP = kCpNt;
 
-// Kernel for a vector width, a tile width (7 or 8 vectors per thread) and a
+// Kernel for a vector width, a tile width (4, 7 or 8 vectors per thread) and a
 // count source, as a table: (VB, U, DEVN) are template arguments.
 template <template <int, int, bool> class K>
 const void* pick_kernel(int vec_bytes, int u, bool devn) {
 #define MOE_EP_PICK(VB) \
   case VB: \
     if (u == 8) return devn ? K<VB, 8, true>::fn() : K<VB, 8, false>::fn(); \
+    if (u == 4) return devn ? K<VB, 4, true>::fn() : K<VB, 4, false>::fn(); \
     return devn ? K<VB, 7, true>::fn() : K<VB, 7, false>::fn();
   switch (vec_bytes) {
     MOE_EP_PICK(16) MOE_EP_PICK(8) MOE_EP_PICK(4) MOE_EP_PICK(2) MOE_EP_PICK(1)

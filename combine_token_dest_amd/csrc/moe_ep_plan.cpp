@@ -42,8 +42,21 @@ LaunchShape row_tile(int64_t rows, int64_t nv) {
   return best;
 }
 
+// Source-row order.  Rows of up to 512 vectors (8 KiB of 16-byte vectors)
+// take two-wave workgroups of 4 vectors per thread instead of one wave of 7
+// or 8 when all of those workgroups are resident at once (MI355X: 256 CUs x
+// 32 waves): 3% faster on a 16-rank round of 7 KiB rows and 2% on an
+// 8-rank ragged one, but 6% slower on a 32-rank round of 8 KiB rows, whose
+// 8192 rows would need two passes.
+constexpr int64_t kResidentWaves = 256 * 32;
+
 LaunchShape dispatch_shape(int64_t rows, int64_t hidden_bytes, int vec_bytes) {
-  return row_tile(rows, hidden_bytes / vec_bytes);
+  const int64_t nv = hidden_bytes / vec_bytes;
+  if (nv > 256 && nv <= 512 && rows * 2 <= kResidentWaves) {
+    const int block = round_block(std::min<int64_t>(kDispatchBlock, (nv + 3) / 4), kMaxBlock);
+    return LaunchShape{(int)rows, 1, block, 4};
+  }
+  return row_tile(rows, nv);
 }
 
 LaunchShape combine_shape(int64_t tokens, int64_t hidden, int vec_elems) {

@@ -76,6 +76,11 @@ int main() {
     expect(t.u == 7 || t.u == 8, "tile u");
     expect(t.block % 64 == 0 && t.block <= moe_ep_detail::kDispatchBlock, "tile block");
     expect((int64_t)t.grid_y * t.block * t.u >= nv || t.grid_y == moe_ep_detail::kMaxGridY, "tile covers the row");
+    for (int64_t rows : {1, 4096, 8192}) {
+      const LaunchShape d = moe_ep_detail::dispatch_shape(rows, nv * 16, 16);
+      expect(d.u == 4 || d.u == 7 || d.u == 8, "dispatch tile u");
+      expect((int64_t)d.grid_y * d.block * d.u >= nv || d.grid_y == moe_ep_detail::kMaxGridY, "dispatch covers the row");
+    }
     const LaunchShape c = moe_ep_detail::combine_shape(5, nv, 1);
     expect((int64_t)c.grid_y * c.block * c.u >= nv || c.grid_y == moe_ep_detail::kMaxGridY, "combine covers the row");
   }

@@ -1,0 +1,52 @@
+"""bench.py on the CPU: its byte accounting and its command-line contract.
+
+The algorithmic bytes behind the reported GB/s and roofline are checked on a
+hand-counted step, and the routed-pair count against the oracle's own
+placement of the DeepSeek-V3-shaped workload.  No GPU is used.
+"""
+
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from types import SimpleNamespace
+
+import numpy as np
+
+import bench
+import oracle
+from synth import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_algorithmic_bytes_hand_counted():
+    # 2 ranks, top_k 2, 100-byte rows, 8-byte scales, 10-element bf16 output
+    # rows; 3 real tokens reaching 1, 2 and 0 ranks (3 routed pairs); tpr 2.
+    w = SimpleNamespace(top_k=2, hidden_row_bytes=100, scale_row_bytes=8, hidden_size=10,
+                        combine_elem_bytes=2, ep_size=2)
+    b_d, b_c, N, P, R = bench.algorithmic_bytes(w, [2, 1], [0b01, 0b11, 0b00], 2, True)
+    assert (N, P, R) == (3, 3, 8)
+    reads = 3 * (4 * 2 * 2 + 100 + 8)       # ids + weights + hidden + scale of each real token
+    writes = 3 * (100 + 8) + 8 * 4 * 2 * 2  # routed rows + the ids/weights slot of every receive row
+    assert b_d == reads + writes
+    assert b_c == 3 * 20 + 3 * 20           # routed expert rows in, output rows out
+
+
+def test_routed_pairs_match_the_oracle():
+    w = wl.BY_NAME["dsv3"]
+    inp = wl.make_inputs(w)
+    masks = bench.destination_masks(w, inp)
+    p = oracle.Params(w.ep_size, w.num_experts, w.top_k, w.max_tokens_per_rank, w.hidden_size,
+                      w.hidden_row_bytes)
+    res = oracle.OracleMoEEp(p).dispatch(inp.hidden, inp.topk_ids, inp.topk_weights)
+    routed = sum(int(r.valid.sum()) for r in res)
+    assert sum(bin(m).count("1") for m in masks) == routed
+
+
+def test_more_than_one_gpu_is_refused():
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert p.returncode == 2
+    assert "one GPU" in p.stderr

@@ -125,6 +125,7 @@ constexpr int kDispatchBlock = 128;      // dispatch threads per workgroup, at m
 constexpr int kCombineU = 1;             // combine: vectors per thread
 constexpr int kCombineDB = 8;            // combine: destination rows loaded per batch
 constexpr int kCombineBlock = 1024;      // combine threads per workgroup, at most
+constexpr int kCombineSmallBatchMaxBlock = 512;   // combine: half batches for low fan-out up to this
 
 struct LaunchShape {
   int grid_x;   // rows (dispatch) or real tokens (combine)

@@ -399,6 +399,30 @@ def main():
     torch.cuda.synchronize()
     wall_plain = time.perf_counter() - t2
 
+    # The same rounds replayed from HIP graphs (one captured dispatch +
+    # combine per instance): what a caller that captures the round sees.
+    graph_us = None
+    try:
+        graphs = []
+        for inst in insts:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                cs = torch.cuda.current_stream(device).cuda_stream
+                inst.dispatch(cs)
+                inst.combine(cs)
+            graphs.append(g)
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        t3 = time.perf_counter()
+        for i in range(K):
+            graphs[i % I].replay()
+        torch.cuda.synchronize()
+        graph_us = round((time.perf_counter() - t3) / K * 1e6, 2)
+        del graphs
+    except Exception as e:          # reported, never fatal: this is an extra
+        log(f"[bench] graph replay skipped: {e}")
+
     ms_step = wall_plain / K * 1e3
     value = bytes_round / (wall_plain / K) / 1e9
     d_us = float((d_ms * w_g).sum() / w_g.sum() * 1e3)
@@ -472,6 +496,7 @@ def main():
                                "bytes": b_c, "GB/s": round(c_gbs, 1)},
         },
         "us_per_round_grouped_with_events": round(wall_s / K * 1e6, 2),
+        "us_per_round_graph_replay": graph_us,
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": dom_bytes,

@@ -171,6 +171,9 @@ EDGE = [
     ("ids_out_of_range", dict(ep=4, E=8, K=4, cap=10, n=[10, 10, 10, 10], hidden_size=64, H=128,
                               id_lo=-3, id_hi=12)),
     ("invalid_is_E", dict(ep=4, E=8, K=2, cap=10, n=[10, 0, 10, 3], hidden_size=64, H=128, invalid=8)),
+    # every token reaches no rank: combine writes zeros without loading a row
+    ("no_token_reaches_a_rank", dict(ep=4, E=8, K=3, cap=10, n=[10, 3, 0, 7], hidden_size=64, H=128,
+                                     id_lo=-5, id_hi=0, dtype="f32")),
     ("mask_some", dict(ep=8, E=64, K=6, cap=40, n=[40, 39, 0, 1, 2, 40, 13, 7], hidden_size=512, H=1024,
                        mask=0b10110101)),
     ("mask_none_active", dict(ep=4, E=8, K=2, cap=8, n=[8, 8, 8, 8], hidden_size=32, H=64, mask=0)),

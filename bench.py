@@ -402,6 +402,7 @@ def main():
     # The same rounds replayed from HIP graphs (one captured dispatch +
     # combine per instance): what a caller that captures the round sees.
     graph_us = None
+    graph_all_us = None
     try:
         graphs = []
         for inst in insts:
@@ -420,6 +421,23 @@ def main():
         torch.cuda.synchronize()
         graph_us = round((time.perf_counter() - t3) / K * 1e6, 2)
         del graphs
+        # All I rounds in one graph (2*I kernel nodes): the per-launch cost
+        # of a graph is then spread over I rounds.
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream(device).cuda_stream
+            for inst in insts:
+                inst.dispatch(cs)
+                inst.combine(cs)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, K // I)
+        t4 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_all_us = round((time.perf_counter() - t4) / (reps * I) * 1e6, 2)
+        del g
     except Exception as e:          # reported, never fatal: this is an extra
         log(f"[bench] graph replay skipped: {e}")
 
@@ -497,6 +515,7 @@ def main():
         },
         "us_per_round_grouped_with_events": round(wall_s / K * 1e6, 2),
         "us_per_round_graph_replay": graph_us,
+        "us_per_round_graph_replay_all_instances": graph_all_us,
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": dom_bytes,

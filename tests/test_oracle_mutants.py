@@ -54,6 +54,31 @@ MUTANTS = [
     ("scale rows not copied", "moe_ep.py", "                            out_scale[r] = scl_s[t]",
      "                            out_scale[r] = 0"),
     ("hidden row off by one", "moe_ep.py", "out_hidden[r] = hid_s[t]", "out_hidden[r] = hid_s[max(t - 1, 0)]"),
+    ("invalid id fixed at -1", "moe_ep.py",
+     "out_ids[r] = p.invalid_expert_id", "out_ids[r] = -1"),
+    ("combine reads the transposed row", "moe_ep.py",
+     "                r = s * tpr + t\n                acc = np.zeros",
+     "                r = t * ep + s\n                acc = np.zeros"),
+    ("combine skips the last rank", "moe_ep.py",
+     "for d in range(ep):                      # ascending rank order", "for d in range(ep - 1):"),
+    ("f32 combine rounded through bf16", "moe_ep.py",
+     "out[t] = acc if dtype == \"f32\"",
+     "out[t] = bf16_bits_to_f32(f32_to_bf16_bits_rne(acc)) if dtype == \"f32\""),
+    ("negative ids routed to rank 0", "moe_ep.py",
+     "    if 0 <= expert_id < params.num_experts:\n",
+     "    if expert_id < params.num_experts:\n        expert_id = max(expert_id, 0)\n"),
+    ("call state kept after combine", "moe_ep.py",
+     "            outputs.append(out)\n        self.record = None\n",
+     "            outputs.append(out)\n"),
+    ("statistics gathered to rank 0 only", "moe_ep.py",
+     "None if gathered is None else gathered.copy()",
+     "None if gathered is None else (gathered.copy() if d == 0 else np.zeros_like(gathered))"),
+    ("weights of routed rows zeroed", "moe_ep.py",
+     "                            out_w[r] = w_s[t]", "                            out_w[r] = 0.0"),
+    ("bf16 widened by an 8-bit shift", "numerics.py",
+     "<< np.uint32(16)).view(np.float32)", "<< np.uint32(8)).view(np.float32)"),
+    ("bf16 ties rounded away from zero", "numerics.py",
+     "rounded = (u + (np.uint32(0x7FFF) + lsb))", "rounded = (u + np.uint32(0x8000))"),
     ("bf16 by truncation", "numerics.py",
      "def f32_to_bf16_bits_rne(x: np.ndarray) -> np.ndarray:\n",
      "def f32_to_bf16_bits_rne(x: np.ndarray) -> np.ndarray:\n"

@@ -309,8 +309,19 @@ def test_error_rules():
         o.dispatch(hid, ids, w)
     assert e.value.kind == "state"
     o.combine([np.zeros((4, 2), np.float32)] * 2, "f32")
+    # The pair is done: a second combine has nothing to combine, and the
+    # next dispatch starts a new pair (one pair in flight at a time).
+    with pytest.raises(OracleError) as e:
+        o.combine([np.zeros((4, 2), np.float32)] * 2, "f32")
+    assert e.value.kind == "state"
+    res = o.dispatch(hid, ids, w)
+    assert res[0].tokens_per_rank == 4
+    o.combine([np.zeros((8, 2), np.float32)] * 2, "f32")
     o.destroy()
     o.destroy()
+    with pytest.raises(OracleError) as e:
+        o.dispatch(hid, ids, w)
+    assert e.value.kind == "state"
 
 
 def test_mask_rules():

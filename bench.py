@@ -25,6 +25,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import dataclasses
 import hashlib
 import json
 import os
@@ -289,6 +290,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--tokens-per-rank", type=int, default=None,
+                    help="the workload at another capacity (tokens per rank), e.g. decode batch sizes")
     ap.add_argument("--instances", type=int, default=8)
     ap.add_argument("--dispatch-order", default="auto", choices=["auto", "source", "destination"],
                     help="copy order of the dispatch kernel (the library picks by shape under auto)")
@@ -298,6 +301,9 @@ def main():
                     help="(default) time a plain 1 GiB device-to-device copy: the PMC byte scale, and the "
                          "measured copy bandwidth the round is compared with")
     ap.add_argument("--no-copy-calibration", action="store_true", help="skip the 1 GiB copy")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP graph replays after the timed passes (profiled runs: the kernel "
+                         "trace then holds only the set-up, warm-up and timed launches)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -321,6 +327,11 @@ def main():
     torch.cuda.set_device(device)
 
     w = wl.BY_NAME[args.workload]
+    if args.tokens_per_rank is not None:
+        if args.tokens_per_rank < 1:
+            print("--tokens-per-rank must be at least 1", file=sys.stderr)
+            sys.exit(2)
+        w = dataclasses.replace(w, max_tokens_per_rank=args.tokens_per_rank)
     log(f"[bench] workload {w.name} seed {w.seed}: generating inputs")
     inp = wl.make_inputs(w)
     to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
@@ -403,43 +414,44 @@ def main():
     # combine per instance): what a caller that captures the round sees.
     graph_us = None
     graph_all_us = None
-    try:
-        graphs = []
-        for inst in insts:
+    if not args.no_graph:
+        try:
+            graphs = []
+            for inst in insts:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    cs = torch.cuda.current_stream(device).cuda_stream
+                    inst.dispatch(cs)
+                    inst.combine(cs)
+                graphs.append(g)
+            for g in graphs:
+                g.replay()
+            torch.cuda.synchronize()
+            t3 = time.perf_counter()
+            for i in range(K):
+                graphs[i % I].replay()
+            torch.cuda.synchronize()
+            graph_us = round((time.perf_counter() - t3) / K * 1e6, 2)
+            del graphs
+            # All I rounds in one graph (2*I kernel nodes): the per-launch cost
+            # of a graph is then spread over I rounds.
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 cs = torch.cuda.current_stream(device).cuda_stream
-                inst.dispatch(cs)
-                inst.combine(cs)
-            graphs.append(g)
-        for g in graphs:
+                for inst in insts:
+                    inst.dispatch(cs)
+                    inst.combine(cs)
             g.replay()
-        torch.cuda.synchronize()
-        t3 = time.perf_counter()
-        for i in range(K):
-            graphs[i % I].replay()
-        torch.cuda.synchronize()
-        graph_us = round((time.perf_counter() - t3) / K * 1e6, 2)
-        del graphs
-        # All I rounds in one graph (2*I kernel nodes): the per-launch cost
-        # of a graph is then spread over I rounds.
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            cs = torch.cuda.current_stream(device).cuda_stream
-            for inst in insts:
-                inst.dispatch(cs)
-                inst.combine(cs)
-        g.replay()
-        torch.cuda.synchronize()
-        reps = max(1, K // I)
-        t4 = time.perf_counter()
-        for _ in range(reps):
-            g.replay()
-        torch.cuda.synchronize()
-        graph_all_us = round((time.perf_counter() - t4) / (reps * I) * 1e6, 2)
-        del g
-    except Exception as e:          # reported, never fatal: this is an extra
-        log(f"[bench] graph replay skipped: {e}")
+            torch.cuda.synchronize()
+            reps = max(1, K // I)
+            t4 = time.perf_counter()
+            for _ in range(reps):
+                g.replay()
+            torch.cuda.synchronize()
+            graph_all_us = round((time.perf_counter() - t4) / (reps * I) * 1e6, 2)
+            del g
+        except Exception as e:          # reported, never fatal: this is an extra
+            log(f"[bench] graph replay skipped: {e}")
 
     ms_step = wall_plain / K * 1e3
     value = bytes_round / (wall_plain / K) / 1e9
@@ -450,7 +462,8 @@ def main():
     dname = "dispatch_dst_kernel" if insts[0].order == "destination" else "dispatch_kernel"
     dominant = dname if d_us >= c_us else "combine_kernel"
     dom_bytes, dom_us, dom_gbs = (b_d, d_us, d_gbs) if dominant == dname else (b_c, c_us, c_gbs)
-    traffic = read_traffic(w.name, dominant)
+    # The counters were taken on the workloads as defined, not at other capacities.
+    traffic = read_traffic(w.name, dominant) if args.tokens_per_rank is None else None
 
     copy_info = None
     if not args.no_copy_calibration:

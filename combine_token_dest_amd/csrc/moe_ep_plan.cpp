@@ -69,23 +69,29 @@ LaunchShape combine_shape(int64_t tokens, int64_t hidden, int vec_elems) {
 
 // Destination-major order: rows per XCD block such that a block's source
 // rows (about 512 KiB) stay in the XCD's L2 while every destination re-reads
-// them.  AUTO takes it for decode-sized groups, where it was ~7% faster on
-// the DeepSeek-V3-shaped dispatch, and the source-row order elsewhere: with
-// 16 or 32 ranks, or 512-token ragged steps, destination-major was 1.7-2x
-// slower (one workgroup per (row, destination), most with nothing to copy).
+// them.  It launches one workgroup per (destination, row), each of which
+// routes its token before storing; that only pays off when the grid holds at
+// least two resident generations of workgroups, so one generation's routing
+// overlaps another's stores.  AUTO takes it then, for groups of at most 16
+// ranks and ep * ep * tpr <= 16384, and the source-row order otherwise.
+// Measured on the DeepSeek-V3 shape (8 ranks, 14 KiB rows; three
+// interleaved runs each): destination-major 3.6% faster at 128 tokens per
+// rank and 9% at 256 (two and four generations), 5.6% and 8.6% slower at 32
+// and 64 (half and one), even at 16 or fewer; with 16 or 32 ranks, or
+// 512-token ragged steps, it was 1.2-2x slower (most of its workgroups copy
+// nothing when a row reaches few of many ranks).
 constexpr int64_t kDmBlockBytes = 512 * 1024;
 constexpr int64_t kDmAutoMaxPairs = 16384;   // ep * ep * tpr
 constexpr int kDmAutoMaxRanks = 16;
+constexpr int64_t kDmAutoMinGenerations = 2;
 
 bool plan_dispatch(DispatchKArgs& a, int vec_bytes, int requested) {
   const int64_t rows = (int64_t)a.ep * a.tpr;
-  int order = requested;
-  if (order == MOE_EP_ORDER_AUTO)
-    order = (a.ep <= kDmAutoMaxRanks && rows * a.ep <= kDmAutoMaxPairs) ? MOE_EP_ORDER_DESTINATION
-                                                                         : MOE_EP_ORDER_SOURCE_ROW;
-  a.order = order;
+  const bool automatic = requested == MOE_EP_ORDER_AUTO;
+  a.order = MOE_EP_ORDER_SOURCE_ROW;
   a.dm_items = 0;
-  if (order != MOE_EP_ORDER_DESTINATION) return true;
+  if (requested == MOE_EP_ORDER_SOURCE_ROW) return true;
+  if (automatic && (a.ep > kDmAutoMaxRanks || rows * a.ep > kDmAutoMaxPairs)) return true;
   const int64_t rmax = (rows + 7) / 8;
   int64_t b = kDmBlockBytes / std::max<int64_t>(1, a.hidden_bytes);
   b = std::max<int64_t>(1, std::min<int64_t>(b, std::max<int64_t>(1, rmax)));
@@ -95,12 +101,13 @@ bool plan_dispatch(DispatchKArgs& a, int vec_bytes, int requested) {
   const int64_t chunks = std::max<int64_t>(1, (nv + (int64_t)tile.block * tile.u - 1) / ((int64_t)tile.block * tile.u));
   // the product is formed in double first: in int64 it can overflow
   const double est = 8.0 * (double)nq * a.ep * (double)b * (double)chunks;
-  const int64_t items = est + a.ep > 2147483647.0 ? 0 : 8 * nq * a.ep * b * chunks;
-  if (est + a.ep > 2147483647.0) {
-    if (requested != MOE_EP_ORDER_AUTO) return false;
-    a.order = MOE_EP_ORDER_SOURCE_ROW;
-    return true;
+  if (est + a.ep > 2147483647.0) return automatic;     // AUTO falls back to the source-row order
+  const int64_t items = 8 * nq * a.ep * b * chunks;
+  if (automatic) {
+    const int64_t resident = kResidentWaves / ((tile.block + 63) / 64);   // workgroups on the chip at once
+    if (items < kDmAutoMinGenerations * resident) return true;
   }
+  a.order = MOE_EP_ORDER_DESTINATION;
   a.dm_block_rows = (int32_t)b;
   a.dm_blocks = (int32_t)nq;
   a.dm_chunks = (int32_t)chunks;

@@ -69,9 +69,13 @@ typedef enum moe_ep_status {
  *  DESTINATION: a workgroup writes one (destination, row) pair; rows are
  *               pinned to XCDs so the other destinations' re-reads of a row
  *               hit that XCD's L2, and each destination's region is written
- *               as one sequential sweep (best for decode-sized groups).
- *  AUTO:        DESTINATION when ep_size <= 16 and ep_size^2 * tokens_per_rank
- *               <= 16384, else SOURCE_ROW.
+ *               as one sequential sweep (best for small groups whose
+ *               (destination, row) workgroups fill the chip several times).
+ *  AUTO:        DESTINATION when ep_size <= 16, ep_size^2 * tokens_per_rank
+ *               <= 16384 and the destination-major grid holds at least twice
+ *               as many workgroups as MI355X runs at once (256 CUs x 32 waves,
+ *               two waves per workgroup for 14 KiB rows: 8192), else
+ *               SOURCE_ROW.
  * An explicit DESTINATION request whose grid would pass 2^31 - 1 workgroups
  * makes moe_ep_dispatch fail with MOE_EP_ERR_INVALID_ARG (nothing launched);
  * AUTO then takes SOURCE_ROW instead. */

@@ -85,6 +85,45 @@ int main() {
     expect((int64_t)c.grid_y * c.block * c.u >= nv || c.grid_y == moe_ep_detail::kMaxGridY, "combine covers the row");
   }
 
+  // The copy order AUTO picks: destination-major for groups of at most 16
+  // ranks, ep * ep * tpr <= 16384 and at least two resident generations of
+  // (destination, row) workgroups; else source-row.
+  struct OrderCase { int ep, tpr; int64_t row_bytes; int requested, expect; };
+  const OrderCase order_cases[] = {
+      {8, 128, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION},    // DeepSeek-V3 decode round
+      {8, 256, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION},
+      {8, 64, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},      // one generation
+      {8, 32, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},
+      {8, 1, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},
+      {8, 512, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},     // ep * ep * tpr > 16384
+      {8, 128, 8192, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},      // one-wave tiles: one generation
+      {4, 512, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION},
+      {16, 32, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION},
+      {16, 256, 7168, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},     // 16-rank fp8 round
+      {32, 256, 8192, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},     // more than 16 ranks
+      {4, 16, 512, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},
+      {4, 16, 512, MOE_EP_ORDER_DESTINATION, MOE_EP_ORDER_DESTINATION},
+      {8, 0, 14336, MOE_EP_ORDER_DESTINATION, MOE_EP_ORDER_DESTINATION},
+      {8, 128, 14336, MOE_EP_ORDER_SOURCE_ROW, MOE_EP_ORDER_SOURCE_ROW},
+  };
+  for (const OrderCase& oc : order_cases) {
+    moe_ep_detail::DispatchKArgs k;
+    std::memset(&k, 0, sizeof(k));
+    k.ep = oc.ep;
+    k.tpr = oc.tpr;
+    k.hidden_bytes = oc.row_bytes;
+    expect(moe_ep_detail::plan_dispatch(k, 16, oc.requested), "plan_dispatch");
+    expect(k.order == oc.expect, "dispatch order");
+    if (k.order == MOE_EP_ORDER_DESTINATION) {
+      // every (destination, row, chunk) item of the decode exists
+      expect(k.dm_items == 8LL * k.dm_blocks * k.ep * k.dm_block_rows * k.dm_chunks, "item count");
+      expect(8LL * k.dm_blocks * k.dm_block_rows >= (int64_t)k.ep * k.tpr, "blocks cover the rows");
+      expect((int64_t)k.dm_chunks * k.dm_threads * k.dm_u * 16 >= oc.row_bytes, "chunks cover the row");
+    } else {
+      expect(k.dm_items == 0, "no destination-major items");
+    }
+  }
+
   // Validation paths of one handle over a fake workspace.
   moe_ep_params p = base();
   expect(moe_ep_workspace_bytes(&p, &n) == MOE_EP_OK, "workspace_bytes");

@@ -5,6 +5,7 @@ Every test prints the case it runs before touching the GPU.
 
 from __future__ import annotations
 
+import dataclasses
 import zlib
 
 import numpy as np
@@ -44,6 +45,26 @@ def test_workload_full_size(name, order):
     log(f"[parity] workload {name} seed {w.seed} order {order}")
     c = parity.case_from_workload(w)
     parity.run_step(c, zero_copy=True, order=order)
+
+
+@pytest.mark.parametrize("tpr", [1, 3, 32, 64, 256])
+def test_dsv3_shape_at_decode_capacities(tpr):
+    """The DeepSeek-V3 shape (8 ranks, 14 KiB rows) at other capacities: the
+    destination-major grid from a fraction of one XCD block up to four
+    resident generations, and the source-row grid from 8 rows up, both
+    orders and AUTO.  At 32 tokens per rank a ragged step also runs under a
+    runtime bound of 5."""
+    w = dataclasses.replace(wl.BY_NAME["dsv3"], max_tokens_per_rank=tpr)
+    c = parity.case_from_workload(w, seed=9000 + tpr)
+    for order in ORDERS + ["auto"]:
+        log(f"[parity] dsv3 shape tpr {tpr} order {order}")
+        parity.run_step(c, zero_copy=order != "source", order=order)
+    if tpr == 32:
+        c = parity.case_from_workload(w, local_num_tokens=[5, 0, 1, 2, 0, 5, 3, 0], seed=9100)
+        c.rtpr = 5
+        for order in ORDERS:
+            log(f"[parity] dsv3 shape tpr 32, runtime bound 5, ragged, order {order}")
+            parity.run_step(c, zero_copy=True, order=order)
 
 
 @pytest.mark.parametrize("name,expect", [("tiny", "source"), ("dsv3", "destination"),

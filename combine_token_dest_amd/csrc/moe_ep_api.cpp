@@ -155,6 +155,8 @@ struct moe_ep_handle_s {
   moe_ep_params p;
   Layout L;
   uint8_t* ws;
+  int device;          // device holding the workspace, or -1 when HIP cannot tell
+  void* checked_stream;  // last non-null stream found on `device`
   OwnerDiv owner;
   int state;
   // Remembered from the dispatch for its combine.
@@ -213,6 +215,37 @@ int vmm_unmap(VmmWorkspace& v) {
     v.broken = true;
     return fail(MOE_EP_ERR_HIP, "hipMemRelease: %s", hipGetErrorString(e));
   }
+  return MOE_EP_OK;
+}
+
+// Device of a workspace pointer, or -1 when HIP does not know the pointer.
+int workspace_device(const void* ws) {
+  hipPointerAttribute_t attr;
+  std::memset(&attr, 0, sizeof(attr));
+  if (hipPointerGetAttributes(&attr, ws) != hipSuccess) {
+    (void)hipGetLastError();          // leave no sticky error for the caller's next call
+    return -1;
+  }
+  return attr.type == hipMemoryTypeDevice ? attr.device : -1;
+}
+
+// The launch would run on the device that holds the workspace: the stream's
+// device, or the current device for the null stream.  A definite mismatch
+// is refused before anything is enqueued (the kernels would touch another
+// device's memory); when HIP cannot tell, the call goes ahead.
+int check_launch_device(moe_ep_handle h, void* stream) {
+  if (h->device < 0) return MOE_EP_OK;
+  if (stream && stream == h->checked_stream) return MOE_EP_OK;   // a stream keeps its device
+  int dev = -1;
+  const hipError_t e = stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_EP_OK;
+  }
+  if (dev != h->device)
+    return fail(MOE_EP_ERR_INVALID_ARG, "the stream runs on device %d but the workspace is on device %d", dev,
+                h->device);
+  if (stream) h->checked_stream = stream;
   return MOE_EP_OK;
 }
 
@@ -284,6 +317,8 @@ int moe_ep_create(const moe_ep_params* params, void* workspace, size_t workspace
   h->L = L;
   h->ws = static_cast<uint8_t*>(workspace);
   h->owner = make_owner_div((uint32_t)(params->num_experts / params->ep_size));
+  h->device = workspace_device(workspace);
+  h->checked_stream = nullptr;
   h->state = kIdle;
   h->tpr = 0;
   h->mask = MOE_EP_ALL_RANKS;
@@ -340,6 +375,7 @@ int moe_ep_create_vmm(const moe_ep_params* params, moe_ep_handle* out_handle) {
     return st;
   }
   h->vmm = v;
+  h->device = v.device;
   *out_handle = h;
   return ok();
 }
@@ -513,6 +549,8 @@ int moe_ep_dispatch(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispa
 
   if (!plan_dispatch(k, vec_bytes, p.dispatch_order))
     return fail(MOE_EP_ERR_INVALID_ARG, "destination-order dispatch grid too large for this step");
+  st = check_launch_device(h, stream);
+  if (st != MOE_EP_OK) return st;
   const hipError_t e = launch_dispatch(k, vec_bytes, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MOE_EP_ERR_HIP, "dispatch launch failed: %s", hipGetErrorString(e));
 
@@ -607,6 +645,8 @@ int moe_ep_combine(moe_ep_handle h, const moe_ep_combine_args* a, void* stream) 
   k.hidden = p.hidden_size;
   k.tpr = h->tpr;
   k.ep = ep;
+  st = check_launch_device(h, stream);
+  if (st != MOE_EP_OK) return st;
 
   const hipError_t e = launch_combine(k, a->dtype, vec_elems < 1 ? 1 : vec_elems, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MOE_EP_ERR_HIP, "combine launch failed: %s", hipGetErrorString(e));

@@ -24,9 +24,11 @@
  *   - Validation happens on the host before anything is enqueued.  On any
  *     error no device work is queued and the handle's state is unchanged.
  *   - Device work is enqueued on `stream` (a hipStream_t; NULL = the null
- *     stream) and is asynchronous: inputs must stay valid, and outputs must
- *     not be read, until the stream has passed the call.  No entry point
- *     synchronizes the device or allocates device memory.
+ *     stream of the current device) and is asynchronous: inputs must stay
+ *     valid, and outputs must not be read, until the stream has passed the
+ *     call.  No entry point synchronizes the device or allocates device
+ *     memory.  A stream on another device than the workspace's makes
+ *     dispatch and combine fail with MOE_EP_ERR_INVALID_ARG.
  *   - A handle serves one in-flight dispatch/combine pair and is not
  *     thread-safe.
  *   - Every entry point returns a moe_ep_status (0 = success) unless stated.

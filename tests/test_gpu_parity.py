@@ -264,6 +264,36 @@ def test_random_small_configs():
             parity.run_step(c, zero_copy=order == "source", order=order)
 
 
+def random_larger_config(seed):
+    """A random step with model-sized rows: up to 16 ranks and 64 tokens per
+    rank, rows of 1-14 KiB (odd element counts too), fp8-style scale rows."""
+    rng = np.random.default_rng(seed)
+    ep = int(rng.integers(1, 17))
+    K = int(rng.integers(1, 11))
+    E = ep * int(rng.integers(1, 9))
+    cap = int(rng.integers(0, 65))
+    n = [int(rng.integers(0, cap + 1)) if rng.random() < 0.85 else 0 for _ in range(ep)]
+    hidden_size = int(rng.choice([1024, 2048, 4096, 7168, 7169]))
+    H = int(rng.choice([hidden_size * 2, hidden_size, 14336, 8192, 7168 + 16]))
+    S = int(rng.choice([0, 0, 224, 56]))
+    rtpr = None if rng.random() < 0.5 else int(rng.integers(max(n + [0]), cap + 1))
+    mask = int(rng.integers(0, 1 << ep)) if ep > 1 and rng.random() < 0.3 else None
+    return dict(ep=ep, E=E, K=K, cap=cap, n=n, hidden_size=hidden_size, H=H, S=S, rtpr=rtpr, mask=mask,
+                dtype="f32" if rng.random() < 0.2 else "bf16", weights=rng.random() < 0.9,
+                invalid=-1, id_lo=-1, id_hi=E + 1, eplb=int(rng.choice([0, 0, 64])))
+
+
+def test_random_larger_configs():
+    """30 seeded random steps with model-sized rows, both dispatch orders."""
+    for seed in range(30):
+        kw = random_larger_config(seed)
+        c = random_case(8000 + seed, name=f"larger{seed}", **kw)
+        for order in ORDERS:
+            log(f"[parity] random larger config {seed} order {order}: ep={kw['ep']} K={kw['K']} "
+                f"n={kw['n']} H={kw['H']} S={kw['S']} hidden={kw['hidden_size']} {kw['dtype']}")
+            parity.run_step(c, zero_copy=order == "destination", order=order)
+
+
 def test_misaligned_rows_use_narrow_vectors():
     """Row pointers offset by 1, 2, 4 and 8 bytes from 16-byte alignment."""
     for off in (1, 2, 4, 8):

@@ -6,7 +6,7 @@ names and ``MoEEp`` gives it the flashinfer.moe_ep API shape over torch
 tensors, one list entry per rank.
 """
 
-from ._lib import (MOE_EP_ALL_RANKS, MOE_EP_BF16, MOE_EP_F32, MOE_EP_MAX_RANKS, MOE_EP_ORDER_AUTO,
+from ._lib import (MOE_EP_ALL_RANKS, MOE_EP_BF16, MOE_EP_F16, MOE_EP_F32, MOE_EP_MAX_RANKS, MOE_EP_ORDER_AUTO,
                    MOE_EP_ORDER_DESTINATION, MOE_EP_ORDER_SOURCE_ROW, MoeEpError,
                    moe_ep_active_rank_mask, moe_ep_checkpoint_prepare, moe_ep_checkpoint_restore,
                    moe_ep_combine, moe_ep_create, moe_ep_create_vmm, moe_ep_destroy, moe_ep_dispatch,
@@ -15,7 +15,7 @@ from ._lib import (MOE_EP_ALL_RANKS, MOE_EP_BF16, MOE_EP_F32, MOE_EP_MAX_RANKS, 
 from .moe_ep import DispatchResult, MoEEp
 
 __all__ = [
-    "MOE_EP_ALL_RANKS", "MOE_EP_BF16", "MOE_EP_F32", "MOE_EP_MAX_RANKS", "MOE_EP_ORDER_AUTO",
+    "MOE_EP_ALL_RANKS", "MOE_EP_BF16", "MOE_EP_F16", "MOE_EP_F32", "MOE_EP_MAX_RANKS", "MOE_EP_ORDER_AUTO",
     "MOE_EP_ORDER_DESTINATION", "MOE_EP_ORDER_SOURCE_ROW", "MoeEpError",
     "moe_ep_active_rank_mask", "moe_ep_checkpoint_prepare", "moe_ep_checkpoint_restore",
     "moe_ep_combine", "moe_ep_create", "moe_ep_create_vmm", "moe_ep_destroy", "moe_ep_dispatch",

@@ -26,6 +26,7 @@ MOE_EP_ERR_UNSUPPORTED = -7
 
 MOE_EP_F32 = 0
 MOE_EP_BF16 = 1
+MOE_EP_F16 = 2
 
 MOE_EP_ORDER_AUTO = 0
 MOE_EP_ORDER_SOURCE_ROW = 1

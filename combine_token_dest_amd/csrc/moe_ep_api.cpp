@@ -47,6 +47,16 @@ int64_t align_up(int64_t x, int64_t a) {
 
 enum State { kIdle = 0, kDispatched = 1 };
 
+// Bytes of a combine element type, 0 for an unknown one.
+int dtype_bytes(int dtype) {
+  switch (dtype) {
+    case MOE_EP_F32: return 4;
+    case MOE_EP_BF16: return 2;
+    case MOE_EP_F16: return 2;
+    default: return 0;
+  }
+}
+
 uint64_t rank_bits(int ep) {
   return ep >= 64 ? ~0ull : ((1ull << ep) - 1);
 }
@@ -580,7 +590,7 @@ int moe_ep_get_combine_input_buffer(moe_ep_handle h, int32_t rank, int32_t dtype
   if (h->state != kDispatched)
     return fail(MOE_EP_ERR_STATE, "the combine input buffer is valid only between dispatch and combine");
   if (rank < 0 || rank >= h->p.ep_size) return fail(MOE_EP_ERR_INVALID_ARG, "rank %d outside [0, %d)", rank, h->p.ep_size);
-  const int esz = dtype == MOE_EP_F32 ? 4 : dtype == MOE_EP_BF16 ? 2 : 0;
+  const int esz = dtype_bytes(dtype);
   if (esz == 0) return fail(MOE_EP_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   if (esz > h->p.combine_max_elem_bytes)
     return fail(MOE_EP_ERR_INVALID_ARG, "dtype of %d bytes exceeds combine_max_elem_bytes %d", esz,
@@ -601,7 +611,7 @@ int moe_ep_combine(moe_ep_handle h, const moe_ep_combine_args* a, void* stream) 
   if (a->active_rank_mask != h->mask)
     return fail(MOE_EP_ERR_MASK, "combine active_rank_mask 0x%llx differs from dispatch's 0x%llx",
                 (unsigned long long)a->active_rank_mask, (unsigned long long)h->mask);
-  const int esz = a->dtype == MOE_EP_F32 ? 4 : a->dtype == MOE_EP_BF16 ? 2 : 0;
+  const int esz = dtype_bytes(a->dtype);
   if (esz == 0) return fail(MOE_EP_ERR_INVALID_ARG, "unknown dtype %d", a->dtype);
 
   const uint64_t active = (h->mask == MOE_EP_ALL_RANKS ? ~0ull : h->mask) & rank_bits(ep);

@@ -446,6 +446,7 @@ dispatch_dst_kernel(const DispatchKArgs a) {
 template <int DT, int VE> struct CVec;
 template <int VE> struct CVec<MOE_EP_F32, VE> { typedef typename Bytes<VE * 4>::type type; };
 template <int VE> struct CVec<MOE_EP_BF16, VE> { typedef typename Bytes<VE * 2>::type type; };
+template <int VE> struct CVec<MOE_EP_F16, VE> { typedef typename Bytes<VE * 2>::type type; };
 
 // acc += v (widened to float32) when `use`, else acc += +0.0.  The
 // accumulator starts at +0.0 and a round-to-nearest sum is -0.0 only when
@@ -459,6 +460,12 @@ __device__ __forceinline__ void unpack_add(const typename CVec<DT, VE>::type& v,
     __builtin_memcpy(w, &v, sizeof(w));
 #pragma unroll
     for (int i = 0; i < VE; ++i) acc[i] = acc[i] + (use ? __uint_as_float(w[i]) : 0.0f);
+  } else if constexpr (DT == MOE_EP_F16) {
+    // binary16 -> float32 is exact (v_cvt_f32_f16).
+    uint16_t h[VE];
+    __builtin_memcpy(h, &v, sizeof(h));
+#pragma unroll
+    for (int i = 0; i < VE; ++i) acc[i] = acc[i] + (use ? (float)__builtin_bit_cast(_Float16, h[i]) : 0.0f);
   } else if constexpr (VE == 1) {
     acc[0] = acc[0] + (use ? __uint_as_float((uint32_t)v << 16) : 0.0f);
   } else {
@@ -480,6 +487,13 @@ __device__ __forceinline__ typename CVec<DT, VE>::type pack(const float (&acc)[V
 #pragma unroll
     for (int i = 0; i < VE; ++i) w[i] = __float_as_uint(acc[i]);
     __builtin_memcpy(&v, w, sizeof(w));
+  } else if constexpr (DT == MOE_EP_F16) {
+    // float32 -> binary16, round to nearest even (v_cvt_f16_f32 in the
+    // default rounding mode; overflow gives infinity).
+    uint16_t h[VE];
+#pragma unroll
+    for (int i = 0; i < VE; ++i) h[i] = __builtin_bit_cast(uint16_t, (_Float16)acc[i]);
+    __builtin_memcpy(&v, h, sizeof(h));
   } else {
     // float -> bfloat16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
     uint16_t h[VE];
@@ -669,6 +683,11 @@ hipError_t launch_combine(const CombineKArgs& a, int dtype, int vec_elems, hipSt
   } else if (dtype == MOE_EP_BF16) {
     switch (vec_elems) {
       MOE_EP_C(MOE_EP_BF16, 8) MOE_EP_C(MOE_EP_BF16, 4) MOE_EP_C(MOE_EP_BF16, 2) MOE_EP_C(MOE_EP_BF16, 1)
+      default: return hipErrorInvalidValue;
+    }
+  } else if (dtype == MOE_EP_F16) {
+    switch (vec_elems) {
+      MOE_EP_C(MOE_EP_F16, 8) MOE_EP_C(MOE_EP_F16, 4) MOE_EP_C(MOE_EP_F16, 2) MOE_EP_C(MOE_EP_F16, 1)
       default: return hipErrorInvalidValue;
     }
   } else {

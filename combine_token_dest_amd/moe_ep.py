@@ -19,9 +19,9 @@ from typing import List, Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import MOE_EP_ALL_RANKS, MOE_EP_BF16, MOE_EP_F32
+from ._lib import MOE_EP_ALL_RANKS, MOE_EP_BF16, MOE_EP_F16, MOE_EP_F32
 
-_COMBINE_DTYPES = {torch.float32: MOE_EP_F32, torch.bfloat16: MOE_EP_BF16}
+_COMBINE_DTYPES = {torch.float32: MOE_EP_F32, torch.bfloat16: MOE_EP_BF16, torch.float16: MOE_EP_F16}
 
 
 @dataclass
@@ -247,7 +247,7 @@ class MoEEp:
         """Rank ``rank``'s ``[ep*tpr, hidden]`` buffer in the workspace; valid
         between dispatch and combine.  Passing it to combine saves a copy."""
         if dtype not in _COMBINE_DTYPES:
-            raise TypeError(f"combine dtype must be float32 or bfloat16, got {dtype}")
+            raise TypeError(f"combine dtype must be float32, bfloat16 or float16, got {dtype}")
         ptr = _lib.moe_ep_get_combine_input_buffer(self._handle, rank, _COMBINE_DTYPES[dtype])
         item = torch.empty((), dtype=dtype).element_size()
         return self._view(ptr, self.params.ep_size * self._tpr, self.params.hidden_size * item, dtype)
@@ -269,7 +269,7 @@ class MoEEp:
         if dtype is None:
             dtype = output[0].dtype if output is not None and output[0] is not None else torch.bfloat16
         if dtype not in _COMBINE_DTYPES:
-            raise TypeError(f"combine dtype must be float32 or bfloat16, got {dtype}")
+            raise TypeError(f"combine dtype must be float32, bfloat16 or float16, got {dtype}")
         if self._tpr is None:
             raise _lib.MoeEpError(_lib.MOE_EP_ERR_STATE, "combine", "no dispatch to combine")
         rows = ep * self._tpr

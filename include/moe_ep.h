@@ -87,10 +87,14 @@ typedef enum moe_ep_dispatch_order {
   MOE_EP_ORDER_DESTINATION = 2
 } moe_ep_dispatch_order;
 
-/* Element type of combine's input and output rows (both use the same one). */
+/* Element type of combine's input and output rows (both use the same one;
+ * MoEEpCommunication, get_combine_input_buffer() takes any torch dtype).
+ * Combine widens every element exactly to float32, adds in float32, and
+ * rounds the sum once to the type, to nearest even. */
 typedef enum moe_ep_dtype {
   MOE_EP_F32 = 0,
-  MOE_EP_BF16 = 1
+  MOE_EP_BF16 = 1,
+  MOE_EP_F16 = 2                  /* IEEE binary16 */
 } moe_ep_dtype;
 
 /* Static sizes of one EP group (the pages' MoEEpCommParams plus the
@@ -102,7 +106,8 @@ typedef struct moe_ep_params {
   int32_t top_k;                  /* experts per token, >= 1 */
   int32_t max_tokens_per_rank;    /* capacity: the largest local_num_tokens of any rank */
   int32_t hidden_size;            /* elements of a combine row */
-  int32_t combine_max_elem_bytes; /* element size the combine input buffer is sized for: 2 or 4 */
+  int32_t combine_max_elem_bytes; /* element size the combine input buffer is sized for: 2 (bf16,
+                                     f16) or 4 (also f32) */
   int64_t hidden_row_bytes;       /* bytes of one dispatched hidden_states row (opaque) */
   int64_t scale_row_bytes;        /* bytes of one hidden_states_scale row; 0 = no scales */
   int32_t invalid_expert_id;      /* written into every top_k slot of an invalid receive row */
@@ -213,7 +218,7 @@ MOE_EP_API int moe_ep_get_combine_input_buffer(moe_ep_handle handle, int32_t ran
 /* For every source rank s and token t < n_s: output[s][t] = sum, over the
  * ranks d that token was dispatched to in ascending d, of
  * expert_output[d][s*tpr + t], accumulated in float32 from +0.0 and rounded
- * once to dtype (bfloat16: round to nearest even).  A token that reached no
+ * once to dtype (bfloat16, float16: round to nearest even).  A token that reached no
  * rank gets zeros.  Rows of tokens not dispatched to d are never read, nor is
  * any row of a masked-off rank (MoEEpCommunication, combine();
  * NVLinkOneSidedAlltoAll, combine() mask rule).  Needs the DISPATCHED state;

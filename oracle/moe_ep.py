@@ -34,8 +34,9 @@ Where the pages are silent the oracle takes these readings:
   are still dispatched to the active ranks and still combined;
 * combine adds, in float32, the rows of the ranks the token reached in
   ascending rank order starting from +0.0, then rounds once to the output
-  type (bfloat16 with round-to-nearest-even, or float32 as is); a token that
-  reached no rank gets zeros.
+  type (bfloat16 or float16 with round-to-nearest-even, or float32 as is); a
+  token that reached no rank gets zeros.  The output type is the input's:
+  float32, bfloat16 or float16.
 
 Every loop here is the definition written out, one token or one row at a
 time, so that it can be checked against the pages by eye.
@@ -290,8 +291,10 @@ class OracleMoEEp:
 
         ``expert_output[d]`` is rank d's ``[ep*tpr, hidden]`` or
         ``[ep, tpr, hidden]`` array: float32 for ``dtype="f32"``, bfloat16 bit
-        patterns (uint16) for ``dtype="bf16"``.  Returns per source rank s an
-        ``[n_s, hidden]`` array of the same representation.
+        patterns (uint16) for ``dtype="bf16"``, NumPy float16 for
+        ``dtype="f16"`` (the pages' combine input buffer takes any dtype,
+        MoEEpCommunication, get_combine_input_buffer()).  Returns per source
+        rank s an ``[n_s, hidden]`` array of the same representation.
         """
         p = self.params
         rec = self.record
@@ -300,23 +303,31 @@ class OracleMoEEp:
         mask = _check_mask(p, active_rank_mask)
         if mask != rec.active_rank_mask:
             raise OracleError("mask", "combine mask differs from the dispatch mask")
-        if dtype not in ("f32", "bf16"):
+        if dtype not in ("f32", "bf16", "f16"):
             raise OracleError("invalid_arg", f"dtype {dtype}")
         ep, tpr, hid = p.ep_size, rec.tokens_per_rank, p.hidden_size
         outputs = []
         rows_of = [None if expert_output[d] is None else np.asarray(expert_output[d]).reshape(ep * tpr, hid)
                    for d in range(ep)]
         for s in range(ep):
-            out = np.empty((rec.local_num_tokens[s], hid), np.float32 if dtype == "f32" else np.uint16)
+            out = np.empty((rec.local_num_tokens[s], hid),
+                           {"f32": np.float32, "bf16": np.uint16, "f16": np.float16}[dtype])
             for t in range(rec.local_num_tokens[s]):
                 r = s * tpr + t
                 acc = np.zeros(hid, np.float32)
                 for d in range(ep):                      # ascending rank order
                     if (rec.dest_masks[s][t] >> d) & 1:
                         row = rows_of[d][r]
-                        term = row.astype(np.float32) if dtype == "f32" else bf16_bits_to_f32(row)
+                        # widening to float32 is exact for all three types
+                        term = bf16_bits_to_f32(row) if dtype == "bf16" else row.astype(np.float32)
                         acc = (acc + term).astype(np.float32)
-                out[t] = acc if dtype == "f32" else f32_to_bf16_bits_rne(acc)
+                if dtype == "f32":
+                    out[t] = acc
+                elif dtype == "bf16":
+                    out[t] = f32_to_bf16_bits_rne(acc)
+                else:
+                    with np.errstate(over="ignore"):       # overflow rounds to infinity
+                        out[t] = acc.astype(np.float16)   # NumPy rounds to nearest even
             outputs.append(out)
         self.record = None
         return outputs
@@ -353,5 +364,11 @@ def expert_standin(params: Params, results: Sequence[RankResult],
                 if expert_owner(params, int(res.topk_ids[r, j])) == d:
                     w_local = np.float32(w_local + res.topk_weights[r, j])
             out[r] = (np.asarray(token_values[s][t], np.float32) * w_local).astype(np.float32)
-        outs.append(out if dtype == "f32" else f32_to_bf16_bits_rne(out))
+        if dtype == "f32":
+            outs.append(out)
+        elif dtype == "bf16":
+            outs.append(f32_to_bf16_bits_rne(out))
+        else:
+            with np.errstate(over="ignore"):
+                outs.append(out.astype(np.float16))
     return outs

@@ -183,9 +183,11 @@ def make_inputs(w: Workload, seed: Optional[int] = None, *,
 
 
 def random_rows(rng: np.random.Generator, rows: int, hidden: int, dtype: str) -> np.ndarray:
-    """Standard-normal rows in a combine dtype: float32, or bfloat16 bit
-    patterns (uint16) rounded to nearest even by torch."""
+    """Standard-normal rows in a combine dtype: float32, bfloat16 bit
+    patterns (uint16) or NumPy float16, rounded to nearest even by torch."""
     x = rng.standard_normal((rows, hidden), dtype=np.float32)
     if dtype == "f32":
         return x
+    if dtype == "f16":
+        return torch.from_numpy(x).to(torch.float16).numpy().copy()
     return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()

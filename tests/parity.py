@@ -4,9 +4,9 @@ the CPU oracle on identical seeded inputs, and compare.
 
 Bars (from the method's definition): receive-region ids, weights, and the
 bytes of every routed hidden/scale row are bit-exact; combine outputs are
-within 1e-5 relative (float32) or 2e-2 absolute (bfloat16) of the oracle's,
-and are expected to be bit-identical because both add in float32 in
-ascending rank order and round once.
+within 1e-5 relative (float32), 2e-2 absolute (bfloat16) or 1e-2 absolute
+(float16) of the oracle's, and bit-identical, because both add in float32
+in ascending rank order and round once.
 """
 
 from __future__ import annotations
@@ -21,8 +21,14 @@ import torch
 import oracle
 from synth import workloads as wl
 
+# Combine tolerances.  Both sides add in the same order, so the tests also
+# require identical bits; these bound what a different order could change:
+# float32 relative 1e-5; bfloat16 absolute 2e-2 and float16 absolute 1e-2,
+# above half an ulp for the |sums| < 8 (bfloat16) and < 32 (float16) the
+# tests produce.
 F32_RTOL = 1e-5
 BF16_ATOL = 2e-2
+F16_ATOL = 1e-2
 
 
 def log(msg: str) -> None:
@@ -108,10 +114,10 @@ def combine_inputs_host(c: Case, ores) -> List[np.ndarray]:
     out = []
     for d in range(c.ep):
         a = wl.random_rows(rng, c.ep * ores[d].tokens_per_rank, c.hidden_size, c.combine_dtype)
-        if c.combine_dtype == "f32":
-            a[~ores[d].valid] = np.nan
+        if c.combine_dtype == "bf16":
+            a[~ores[d].valid] = 0x7FC0                 # a bfloat16 NaN
         else:
-            a[~ores[d].valid] = 0x7FC0
+            a[~ores[d].valid] = np.nan
         out.append(a)
     return out
 
@@ -119,11 +125,13 @@ def combine_inputs_host(c: Case, ores) -> List[np.ndarray]:
 def host_to_torch(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
     if dtype == "f32":
         return to_dev(a.astype(np.float32), device)
+    if dtype == "f16":
+        return to_dev(a.astype(np.float16), device)
     return to_dev(a.view(np.int16), device).view(torch.bfloat16)
 
 
 def torch_to_host(t: torch.Tensor, dtype: str) -> np.ndarray:
-    if dtype == "f32":
+    if dtype in ("f32", "f16"):
         return t.cpu().numpy()
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
@@ -167,6 +175,12 @@ def compare_combine(c: Case, gout, oout, tag=""):
             np.testing.assert_allclose(gf, of, rtol=F32_RTOL, atol=0, err_msg=f"{tag} rank {s}")
             np.testing.assert_array_equal(gf.view(np.uint32), of.view(np.uint32),
                                           err_msg=f"{tag} rank {s}: float32 bits")
+        elif c.combine_dtype == "f16":
+            gf, of = g.astype(np.float32), o.astype(np.float32)
+            assert not np.isnan(gf).any(), f"{tag} rank {s}: NaN in output"
+            np.testing.assert_allclose(gf, of, rtol=0, atol=F16_ATOL, err_msg=f"{tag} rank {s}")
+            np.testing.assert_array_equal(g.view(np.uint16), o.view(np.uint16),
+                                          err_msg=f"{tag} rank {s}: float16 bits")
         else:
             gf, of = oracle.bf16_bits_to_f32(g), oracle.bf16_bits_to_f32(o)
             assert not np.isnan(gf).any(), f"{tag} rank {s}: NaN in output"
@@ -193,7 +207,7 @@ def run_step(c: Case, *, zero_copy=True, device="cuda", check=True, moe=None, or
     torch.cuda.synchronize()
     if check:
         compare_dispatch(c, gres, ores, c.name)
-    tdt = torch.float32 if c.combine_dtype == "f32" else torch.bfloat16
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[c.combine_dtype]
     eo_dev = []
     for d in range(c.ep):
         if zero_copy:

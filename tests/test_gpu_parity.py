@@ -67,6 +67,17 @@ def test_dsv3_shape_at_decode_capacities(tpr):
             parity.run_step(c, zero_copy=True, order=order)
 
 
+@pytest.mark.parametrize("order", ORDERS)
+def test_f16_combine_dsv3_shape(order):
+    """The DeepSeek-V3-shaped round with float16 expert outputs: combine
+    widens, adds in float32 and rounds once to float16."""
+    w = wl.BY_NAME["dsv3"]
+    c = parity.case_from_workload(w)
+    c.combine_dtype = "f16"
+    log(f"[parity] dsv3 float16 combine order {order}")
+    parity.run_step(c, zero_copy=order == "destination", order=order)
+
+
 @pytest.mark.parametrize("name,expect", [("tiny", "source"), ("dsv3", "destination"),
                                          ("fp8", "source"), ("ragged", "source")])
 def test_auto_order_choice(name, expect):
@@ -188,6 +199,10 @@ EDGE = [
     ("f32_odd_hidden", dict(ep=4, E=8, K=2, cap=12, n=[12, 5, 0, 11], hidden_size=37, H=148, dtype="f32")),
     ("f32_hidden2", dict(ep=2, E=2, K=1, cap=5, n=[5, 4], hidden_size=2, H=8, dtype="f32")),
     ("bf16_hidden1", dict(ep=3, E=3, K=2, cap=5, n=[5, 4, 3], hidden_size=1, H=2)),
+    ("f16_vec8", dict(ep=4, E=8, K=3, cap=12, n=[12, 5, 0, 11], hidden_size=512, H=1024, dtype="f16")),
+    ("f16_odd_hidden", dict(ep=5, E=10, K=2, cap=9, n=[9, 1, 4, 0, 7], hidden_size=37, H=74, dtype="f16")),
+    ("f16_hidden1_mask", dict(ep=4, E=8, K=2, cap=6, n=[6, 6, 2, 0], hidden_size=1, H=2, dtype="f16",
+                              mask=0b1011)),
     ("scales_odd", dict(ep=4, E=16, K=4, cap=16, n=[16, 3, 0, 9], hidden_size=256, H=256, S=13)),
     ("scales_vec4", dict(ep=4, E=16, K=4, cap=16, n=[16, 3, 0, 9], hidden_size=256, H=256, S=36)),
     ("ids_out_of_range", dict(ep=4, E=8, K=4, cap=10, n=[10, 10, 10, 10], hidden_size=64, H=128,

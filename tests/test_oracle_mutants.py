@@ -62,8 +62,14 @@ MUTANTS = [
     ("combine skips the last rank", "moe_ep.py",
      "for d in range(ep):                      # ascending rank order", "for d in range(ep - 1):"),
     ("f32 combine rounded through bf16", "moe_ep.py",
-     "out[t] = acc if dtype == \"f32\"",
-     "out[t] = bf16_bits_to_f32(f32_to_bf16_bits_rne(acc)) if dtype == \"f32\""),
+     "if dtype == \"f32\":\n                    out[t] = acc\n",
+     "if dtype == \"f32\":\n                    out[t] = bf16_bits_to_f32(f32_to_bf16_bits_rne(acc))\n"),
+    ("f16 combine truncated", "moe_ep.py",
+     "out[t] = acc.astype(np.float16)",
+     "out[t] = (acc.view(np.uint32) & np.uint32(0xFFFFE000)).view(np.float32).astype(np.float16)"),
+    ("f16 combine rounded through bf16", "moe_ep.py",
+     "out[t] = acc.astype(np.float16)",
+     "out[t] = bf16_bits_to_f32(f32_to_bf16_bits_rne(acc)).astype(np.float16)"),
     ("negative ids routed to rank 0", "moe_ep.py",
      "    if 0 <= expert_id < params.num_experts:\n",
      "    if expert_id < params.num_experts:\n        expert_id = max(expert_id, 0)\n"),

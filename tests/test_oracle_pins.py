@@ -178,7 +178,16 @@ def independent_masks(p, inp, active):
     return out
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def _to_dtype(a: np.ndarray, dtype: str) -> np.ndarray:
+    return {"f32": lambda x: x, "bf16": oracle.f32_to_bf16_bits_rne,
+            "f16": lambda x: x.astype(np.float16)}[dtype](a)
+
+
+def _from_dtype(a: np.ndarray, dtype: str) -> np.ndarray:
+    return oracle.bf16_bits_to_f32(a) if dtype == "bf16" else a.astype(np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("mask", [None, 0b1011, 0b0001])
 def test_combine_rank_indicators_sum_to_destination_mask(dtype, mask):
     p, o, res, inp = _dispatch_tiny(mask)
@@ -187,13 +196,52 @@ def test_combine_rank_indicators_sum_to_destination_mask(dtype, mask):
     for d in range(p.ep_size):
         a = np.full((p.ep_size * tpr, p.hidden_size), np.nan, np.float32)
         a[res[d].valid] = float(2 ** d)
-        eo.append(a if dtype == "f32" else oracle.f32_to_bf16_bits_rne(a))
+        eo.append(_to_dtype(a, dtype))
     out = o.combine(eo, dtype, active_rank_mask=mask)
     expect = independent_masks(p, inp, oracle.ALL_RANKS if mask is None else mask)
     for s in range(p.ep_size):
-        got = out[s] if dtype == "f32" else oracle.bf16_bits_to_f32(out[s])
+        got = _from_dtype(out[s], dtype)
         for t in range(inp.local_num_tokens[s]):
             assert (got[t] == float(expect[s][t])).all()
+
+
+def test_f16_combine_rounds_ties_to_even_and_overflows():
+    """Two-rank sums that are exact in float32 and fall halfway between two
+    binary16 values, worked from the format (11 significant bits, largest
+    finite 65504, smallest subnormal 2^-24): 1 + 2^-11 -> 1 (even),
+    1 + 3*2^-11 -> 1 + 2^-9 (even), 65504 + 16 = 65520 -> infinity (the
+    tie goes to the even neighbour 2^16, past the largest finite value),
+    -1 - 2^-11 -> -1; and 2^-24 + 2^-24 = 2^-23 exactly among the
+    subnormals (binary16 values are all multiples of 2^-24, so no sum of
+    them falls between two subnormals)."""
+    p = Params(2, 2, 2, 1, 5, 4)
+    o = OracleMoEEp(p)
+    o.dispatch([np.zeros((1, 4), np.uint8), np.zeros((0, 4), np.uint8)],
+               [np.array([[0, 1]], np.int32), np.zeros((0, 2), np.int32)])
+    a = np.array([[1.0, 1.0 + 2.0 ** -10, 65504.0, -1.0, 2.0 ** -24], [np.nan] * 5], np.float16)
+    b = np.array([[2.0 ** -11, 2.0 ** -11, 16.0, -(2.0 ** -11), 2.0 ** -24], [np.nan] * 5], np.float16)
+    out = o.combine([a, b], "f16")[0][0]
+    bits = out.view(np.uint16)
+    assert bits[0] == 0x3C00                        # 1.0
+    assert bits[1] == 0x3C02                        # 1 + 2^-9
+    assert bits[2] == 0x7C00                        # +infinity
+    assert bits[3] == 0xBC00                        # -1.0
+    assert bits[4] == 0x0002                        # 2^-23
+
+
+def test_f16_rounding_matches_torch_random_sums():
+    """Sums of two random binary16 values rounded to binary16: the oracle's
+    (NumPy) against torch's CPU conversion of the same float32 sums."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((2, 4096)).astype(np.float16)
+    p = Params(2, 2, 2, 1, 4096, 4)
+    o = OracleMoEEp(p)
+    o.dispatch([np.zeros((1, 4), np.uint8), np.zeros((0, 4), np.uint8)],
+               [np.array([[0, 1]], np.int32), np.zeros((0, 2), np.int32)])
+    eo = [np.stack([x[0], x[0]]), np.stack([x[1], x[1]])]
+    out = o.combine(eo, "f16")[0][0]
+    s32 = torch.from_numpy(x[0].astype(np.float32)) + torch.from_numpy(x[1].astype(np.float32))
+    np.testing.assert_array_equal(out.view(np.uint16), s32.to(torch.float16).numpy().view(np.uint16))
 
 
 def test_combine_ones_sum_to_fanout():

@@ -72,14 +72,19 @@ LaunchShape combine_shape(int64_t tokens, int64_t hidden, int vec_elems) {
 // them.  It launches one workgroup per (destination, row), each of which
 // routes its token before storing; that only pays off when the grid holds at
 // least two resident generations of workgroups, so one generation's routing
-// overlaps another's stores.  AUTO takes it then, for groups of at most 16
-// ranks and ep * ep * tpr <= 16384, and the source-row order otherwise.
-// Measured on the DeepSeek-V3 shape (8 ranks, 14 KiB rows; three
-// interleaved runs each): destination-major 3.6% faster at 128 tokens per
-// rank and 9% at 256 (two and four generations), 5.6% and 8.6% slower at 32
-// and 64 (half and one), even at 16 or fewer; with 16 or 32 ranks, or
-// 512-token ragged steps, it was 1.2-2x slower (most of its workgroups copy
-// nothing when a row reaches few of many ranks).
+// overlaps another's stores, and while the source-row grid alone (one
+// routing per row) does not fill the chip.  AUTO takes it then, for groups
+// of at most 16 ranks and ep * ep * tpr <= 16384, and the source-row order
+// otherwise.  Measured with 14 KiB rows (three interleaved runs each):
+//   8 ranks: destination-major 3.6% faster at 128 tokens per rank and 9% at
+//   256 (two and four generations), 5.6% and 8.6% slower at 32 and 64 (half
+//   and one), even at 16 or fewer;
+//   4 ranks: 8.6% faster at 512 tokens, 4% slower at 256 (one generation)
+//   and 4.4% slower at 1024 (4096 source rows fill the chip);
+//   16 ranks: 4.6% and 10% faster at 32 and 64 tokens, even at 16.
+// With 16 ranks and 256 tokens, 32 ranks, or 512-token ragged steps, it was
+// 1.2-2x slower (most of its workgroups copy nothing when a row reaches few
+// of many ranks).
 constexpr int64_t kDmBlockBytes = 512 * 1024;
 constexpr int64_t kDmAutoMaxPairs = 16384;   // ep * ep * tpr
 constexpr int kDmAutoMaxRanks = 16;
@@ -106,6 +111,8 @@ bool plan_dispatch(DispatchKArgs& a, int vec_bytes, int requested) {
   if (automatic) {
     const int64_t resident = kResidentWaves / ((tile.block + 63) / 64);   // workgroups on the chip at once
     if (items < kDmAutoMinGenerations * resident) return true;
+    const LaunchShape src = dispatch_shape(rows, a.hidden_bytes, vec_bytes);
+    if (rows >= kResidentWaves / ((src.block + 63) / 64)) return true;    // the source-row grid fills the chip
   }
   a.order = MOE_EP_ORDER_DESTINATION;
   a.dm_block_rows = (int32_t)b;

@@ -86,8 +86,9 @@ int main() {
   }
 
   // The copy order AUTO picks: destination-major for groups of at most 16
-  // ranks, ep * ep * tpr <= 16384 and at least two resident generations of
-  // (destination, row) workgroups; else source-row.
+  // ranks, ep * ep * tpr <= 16384, at least two resident generations of
+  // (destination, row) workgroups and fewer source rows than fill the chip;
+  // else source-row.
   struct OrderCase { int ep, tpr; int64_t row_bytes; int requested, expect; };
   const OrderCase order_cases[] = {
       {8, 128, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION},    // DeepSeek-V3 decode round
@@ -98,7 +99,11 @@ int main() {
       {8, 512, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},     // ep * ep * tpr > 16384
       {8, 128, 8192, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},      // one-wave tiles: one generation
       {4, 512, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION},
+      {4, 256, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},     // one generation
+      {4, 1024, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},    // 4096 source rows fill the chip
       {16, 32, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION},
+      {16, 64, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION},
+      {16, 16, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},
       {16, 256, 7168, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},     // 16-rank fp8 round
       {32, 256, 8192, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},     // more than 16 ranks
       {4, 16, 512, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},

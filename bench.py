@@ -43,7 +43,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 # The kernels and the host code that picks their launch shapes.
 KERNEL_SOURCES = [os.path.join(ROOT, "combine_token_dest_amd", "csrc", f)
                   for f in ("moe_ep_kernels.hip", "moe_ep_plan.cpp", "moe_ep_internal.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{workload}.txt")
+# PMC summaries are named <workload>_<dispatch kernel>_combine_kernel_traffic.txt
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "{workload}_{dispatch}_combine_kernel_traffic.txt")
 
 
 def log(msg):
@@ -265,10 +266,11 @@ def kernel_source_hash():
     return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
-def read_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` from the committed PMC summary, if it
-    was taken on the current kernel source; else None."""
-    path = TRAFFIC_FILE.format(workload=workload)
+def read_traffic(workload, dispatch_kernel, kernel):
+    """HBM bytes per launch of `kernel` from the committed PMC summary of the
+    workload's round (`dispatch_kernel` + combine_kernel), if it was taken on
+    the current kernel source; else None."""
+    path = TRAFFIC_FILE.format(workload=workload, dispatch=dispatch_kernel)
     if not os.path.exists(path):
         return None
     src_hash = None
@@ -463,7 +465,7 @@ def main():
     dominant = dname if d_us >= c_us else "combine_kernel"
     dom_bytes, dom_us, dom_gbs = (b_d, d_us, d_gbs) if dominant == dname else (b_c, c_us, c_gbs)
     # The counters were taken on the workloads as defined, not at other capacities.
-    traffic = read_traffic(w.name, dominant) if args.tokens_per_rank is None else None
+    traffic = read_traffic(w.name, dname, dominant) if args.tokens_per_rank is None else None
 
     copy_info = None
     if not args.no_copy_calibration:

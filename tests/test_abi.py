@@ -85,6 +85,31 @@ def test_struct_layouts_match_header(lib):
         assert got == int(value), f"{name}.{field}: ctypes {got} vs C {value}"
 
 
+def test_constants_match_header():
+    """Every MOE_EP_* constant of the binding has the header's value, and
+    the header defines no constant the binding lacks."""
+    text = open(HEADER).read()
+    names = sorted(set(re.findall(r"\b(MOE_EP_(?:OK|ERR_\w+|F32|BF16|F16|ORDER_\w+|MAX_RANKS|ALL_RANKS))\b",
+                                  text)))
+    lines = ["#include <stdio.h>", '#include "moe_ep.h"', "int main(void) {"]
+    lines += [f'printf("{n} %llu\\n", (unsigned long long)(long long)({n}));' for n in names
+              if n != "MOE_EP_ALL_RANKS"]
+    lines += ['printf("MOE_EP_ALL_RANKS %llu\\n", (unsigned long long)MOE_EP_ALL_RANKS);', "return 0; }"]
+    with tempfile.TemporaryDirectory() as tmp:
+        src = os.path.join(tmp, "consts.c")
+        exe = os.path.join(tmp, "consts")
+        open(src, "w").write("\n".join(lines))
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), src, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout
+    seen = 0
+    for line in out.splitlines():
+        name, value = line.split()
+        assert hasattr(_lib, name), f"the binding lacks {name}"
+        assert getattr(_lib, name) % (1 << 64) == int(value), f"{name}: binding {getattr(_lib, name)} vs C {value}"
+        seen += 1
+    assert seen == len(names) and seen >= 16
+
+
 def params(**kw):
     base = dict(ep_size=4, num_experts=8, top_k=2, max_tokens_per_rank=16, hidden_size=128,
                 combine_max_elem_bytes=4, hidden_row_bytes=512, scale_row_bytes=0,

@@ -112,6 +112,7 @@ class MoEEp:
         self._n = None
         self._hidden_dtype = None
         self._scale_dtype = None
+        self._buffer_dtype = None      # dtype of the last get_combine_input_buffer() of this round
 
     # -- pages' API --------------------------------------------------------
     @classmethod
@@ -218,6 +219,7 @@ class MoEEp:
         stream = torch.cuda.current_stream(self.device).cuda_stream
         res = _lib.moe_ep_dispatch(self._handle, a, ep, stream)
         self._tpr = res[0].tokens_per_rank if ep else 0
+        self._buffer_dtype = None
         # the copy order the library chose for this step ("source" / "destination")
         self.last_dispatch_order = _ORDER_NAMES.get(res[0].dispatch_order if ep else 0)
         self._n = n
@@ -249,6 +251,7 @@ class MoEEp:
         if dtype not in _COMBINE_DTYPES:
             raise TypeError(f"combine dtype must be float32, bfloat16 or float16, got {dtype}")
         ptr = _lib.moe_ep_get_combine_input_buffer(self._handle, rank, _COMBINE_DTYPES[dtype])
+        self._buffer_dtype = dtype
         item = torch.empty((), dtype=dtype).element_size()
         return self._view(ptr, self.params.ep_size * self._tpr, self.params.hidden_size * item, dtype)
 
@@ -258,7 +261,9 @@ class MoEEp:
         """Sum every token's rows over the ranks it reached; see
         include/moe_ep.h, moe_ep_combine.  ``expert_output[d]`` may be
         ``[ep*tpr, hidden]`` or ``[ep, tpr, hidden]``; None means rank d's
-        combine input buffer."""
+        combine input buffer.  When every entry is None the element type is
+        the output's, else the one last requested from
+        get_combine_input_buffer() this round, else bfloat16."""
         if self._handle is None:
             raise RuntimeError("MoEEp has been destroyed")
         p = self.params
@@ -266,8 +271,11 @@ class MoEEp:
         if len(expert_output) != ep:
             raise ValueError(f"expected {ep} per-rank expert_output tensors")
         dtype = next((t.dtype for t in expert_output if t is not None), None)
-        if dtype is None:
-            dtype = output[0].dtype if output is not None and output[0] is not None else torch.bfloat16
+        if dtype is None:       # every rank's input is its combine input buffer
+            if output is not None and output[0] is not None:
+                dtype = output[0].dtype
+            else:
+                dtype = self._buffer_dtype if self._buffer_dtype is not None else torch.bfloat16
         if dtype not in _COMBINE_DTYPES:
             raise TypeError(f"combine dtype must be float32, bfloat16 or float16, got {dtype}")
         if self._tpr is None:

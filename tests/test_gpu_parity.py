@@ -383,6 +383,31 @@ def test_expert_output_3d_form():
     moe.destroy()
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_combine_of_buffers_only_takes_the_buffer_dtype(dtype):
+    """combine([None] * ep) with no output tensors reads every rank's combine
+    input buffer in the dtype the caller asked that buffer for."""
+    log(f"[parity] combine of the workspace buffers only, {dtype}")
+    c = random_case(6, ep=4, E=8, K=2, cap=9, n=[9, 3, 0, 8], hidden_size=40, H=80, dtype=dtype)
+    p = parity.oracle_params(c)
+    om = oracle.OracleMoEEp(p)
+    ores = om.dispatch(c.hidden, c.ids, c.weights)
+    eo_host = parity.combine_inputs_host(c, ores)
+    oout = om.combine(eo_host, dtype)
+    moe = parity.make_gpu(c)
+    hid, ids, w, _ = parity.upload(c)
+    moe.dispatch(hid, ids, w)
+    tdt = torch.float32 if dtype == "f32" else torch.float16
+    for d in range(c.ep):
+        buf = moe.get_combine_input_buffer(d, tdt)
+        buf.copy_(parity.host_to_torch(eo_host[d], dtype).view(buf.shape))
+    gout = moe.combine([None] * c.ep)
+    torch.cuda.synchronize()
+    assert all(o.dtype == tdt for o in gout)
+    parity.compare_combine(c, gout, oout, "buffers only")
+    moe.destroy()
+
+
 # --------------------------------------------------------------------------
 # Writes stay where the method puts them; reads skip what it never needs
 # --------------------------------------------------------------------------

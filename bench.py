@@ -303,6 +303,9 @@ def main():
                     help="(default) time a plain 1 GiB device-to-device copy: the PMC byte scale, and the "
                          "measured copy bandwidth the round is compared with")
     ap.add_argument("--no-copy-calibration", action="store_true", help="skip the 1 GiB copy")
+    ap.add_argument("--no-two-streams", action="store_true",
+                    help="skip the pass that runs alternate instances' rounds on two streams (profiled "
+                         "runs skip it, with the graph replays)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP graph replays after the timed passes (profiled runs: the kernel "
                          "trace then holds only the set-up, warm-up and timed launches)")
@@ -455,6 +458,27 @@ def main():
         except Exception as e:          # reported, never fatal: this is an extra
             log(f"[bench] graph replay skipped: {e}")
 
+    # The same rounds as two independent streams of work, as a caller that
+    # overlaps two micro-batches would run them: instance j always runs on
+    # stream j % 2 (so each handle's dispatch -> combine order holds), and
+    # one stream's kernel ramps and tails overlap the other's.  Reported
+    # beside `value`, which stays the one-stream round.
+    two_stream_us = None
+    if not args.no_two_streams and I >= 2:
+        streams = [torch.cuda.Stream(device), torch.cuda.Stream(device)]     # default priority
+        def two_stream_rounds(n):
+            for i in range(n):
+                j = i % I
+                cs = streams[j % 2].cuda_stream
+                insts[j].dispatch(cs)
+                insts[j].combine(cs)
+        two_stream_rounds(max(2 * I, args.warmup))       # first launches on new queues are slow
+        torch.cuda.synchronize()
+        t5 = time.perf_counter()
+        two_stream_rounds(K)
+        torch.cuda.synchronize()
+        two_stream_us = round((time.perf_counter() - t5) / K * 1e6, 2)
+
     ms_step = wall_plain / K * 1e3
     value = bytes_round / (wall_plain / K) / 1e9
     d_us = float((d_ms * w_g).sum() / w_g.sum() * 1e3)
@@ -531,6 +555,7 @@ def main():
         "us_per_round_grouped_with_events": round(wall_s / K * 1e6, 2),
         "us_per_round_graph_replay": graph_us,
         "us_per_round_graph_replay_all_instances": graph_all_us,
+        "us_per_round_two_streams": two_stream_us,
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": dom_bytes,

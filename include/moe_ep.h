@@ -186,7 +186,8 @@ MOE_EP_API int moe_ep_workspace_bytes(const moe_ep_params* params, size_t* out_b
 /* Creates a handle over a caller-owned device workspace of at least
  * moe_ep_workspace_bytes() bytes, aligned to 256 bytes.  The workspace is
  * borrowed until moe_ep_destroy and needs no initialisation.  Host-only: no
- * device work. */
+ * device work (it asks HIP which device holds the workspace, so dispatch
+ * and combine can refuse a stream on another device). */
 MOE_EP_API int moe_ep_create(const moe_ep_params* params, void* workspace, size_t workspace_bytes,
                   moe_ep_handle* out_handle);
 

@@ -85,6 +85,12 @@ def test_struct_layouts_match_header(lib):
         assert got == int(value), f"{name}.{field}: ctypes {got} vs C {value}"
 
 
+def test_missing_library_fails_loudly(tmp_path):
+    """No fallback: loading a library that is not there raises."""
+    with pytest.raises(OSError, match="missing"):
+        _lib.load(str(tmp_path / "libmoe_ep.so"))
+
+
 def test_constants_match_header():
     """Every MOE_EP_* constant of the binding has the header's value, and
     the header defines no constant the binding lacks."""

@@ -320,8 +320,11 @@ dispatch_kernel(const DispatchKArgs a) {
 // the same XCD within a short window: the first read comes from HBM, the
 // others from that XCD's L2 (cached loads), while each destination's rows
 // are written as one sequential sweep (nontemporal stores).
+// LEAN: the common step shape -- top_k <= 64, no scale rows, no statistics
+// rows -- without the loops and branches the general one needs; it took
+// ~0.3 us (1.6%) off the DeepSeek-V3-shaped dispatch in interleaved runs.
 // ---------------------------------------------------------------------------
-template <int VB, int U, int SP, bool DEVN>
+template <int VB, int U, int SP, bool DEVN, bool LEAN>
 __device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const int i) {
   typedef typename Bytes<VB>::type V;
   // 32-bit decode: the host keeps the item count below 2^31.
@@ -362,7 +365,21 @@ __device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const 
   // Destination mask of the token (as route_token, written out here: this
   // form measured ~3% faster in this kernel).
   uint64_t m = 0;
-  if (real) {
+  if (LEAN && real) {
+    // top_k <= 64: one id per lane, one pass.
+    const int lane = threadIdx.x & 63;
+    uint64_t bit = 0;
+    if (lane < K) {
+      const uint32_t e = (uint32_t)idr[lane];
+      if (e < (uint32_t)a.num_experts) bit = 1ull << expert_owner(a.owner, e);
+    }
+    for (int jj = 0; jj < K; ++jj) {
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)bit, jj);
+      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(bit >> 32), jj);
+      m |= ((uint64_t)hi << 32) | lo;
+    }
+    m &= a.active;
+  } else if (real) {
     const int lane = threadIdx.x & 63;
     for (int j0 = 0; j0 < K; j0 += 64) {
       uint64_t bit = 0;
@@ -396,8 +413,9 @@ __device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const 
       reinterpret_cast<int32_t*>(part + a.off_ids)[slot] = routed ? idr[jj] : a.invalid_id;
       if (a.has_weights)
         reinterpret_cast<float*>(part + a.off_weights)[slot] = routed ? a.weights[s][(int64_t)t * K + jj] : 0.0f;
+      if (LEAN) break;                       // top_k <= 64 < blockDim.x: one pass
     }
-    if (routed && a.scale_bytes) {
+    if (!LEAN && routed && a.scale_bytes) {
       const int64_t S = a.scale_bytes;
       uint8_t* dst = part + a.off_scale + (int64_t)r * S;
       if (a.scale_vec4) {
@@ -423,12 +441,12 @@ __device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const 
 
 // Grid: x = destination-major item, then one statistics row per source rank
 // when statistics are gathered.
-template <int VB, int U, int SP, bool DEVN>
+template <int VB, int U, int SP, bool DEVN, bool LEAN>
 __global__ void __launch_bounds__(kMaxBlock)
 dispatch_dst_kernel(const DispatchKArgs a) {
   const int i = blockIdx.x;
-  if (i < a.dm_items) {
-    dispatch_dst_item<VB, U, SP, DEVN>(a, i);
+  if (LEAN || i < a.dm_items) {
+    dispatch_dst_item<VB, U, SP, DEVN, LEAN>(a, i);
   } else {
     gather_stats_row(a, i - (int)a.dm_items);
   }
@@ -640,7 +658,10 @@ template <int VB, int U, bool DEVN> struct SourceRowKernel {
   static const void* fn() { return reinterpret_cast<const void*>(&dispatch_kernel<VB, U, kDispatchLP, kDispatchSP, DEVN>); }
 };
 template <int VB, int U, bool DEVN> struct DestinationKernel {
-  static const void* fn() { return reinterpret_cast<const void*>(&dispatch_dst_kernel<VB, U, kDispatchSP, DEVN>); }
+  static const void* fn() { return reinterpret_cast<const void*>(&dispatch_dst_kernel<VB, U, kDispatchSP, DEVN, false>); }
+};
+template <int VB, int U, bool DEVN> struct DestinationLeanKernel {
+  static const void* fn() { return reinterpret_cast<const void*>(&dispatch_dst_kernel<VB, U, kDispatchSP, DEVN, true>); }
 };
 
 hipError_t launch_dispatch(const DispatchKArgs& a, int vec_bytes, hipStream_t stream) {
@@ -650,7 +671,10 @@ hipError_t launch_dispatch(const DispatchKArgs& a, int vec_bytes, hipStream_t st
   dim3 grid, block;
   if (a.order == MOE_EP_ORDER_DESTINATION) {
     if (a.dm_items + extra <= 0) return hipSuccess;
-    fn = pick_kernel<DestinationKernel>(vec_bytes, a.dm_u, devn);
+    // top_k <= 64, no scale rows, no statistics rows: the lean instantiation
+    const bool lean = a.top_k <= 64 && a.scale_bytes == 0 && extra == 0 && a.dm_threads >= 64;
+    fn = lean ? pick_kernel<DestinationLeanKernel>(vec_bytes, a.dm_u, devn)
+              : pick_kernel<DestinationKernel>(vec_bytes, a.dm_u, devn);
     grid = dim3((unsigned)(a.dm_items + extra));
     block = dim3(a.dm_threads);
   } else {

@@ -72,17 +72,6 @@ int64_t pow2_divisor(uint64_t x, int64_t cap) {
   return v;
 }
 
-// Multiply-shift constants for e / d with 0 <= e < 2^31 (Granlund &
-// Montgomery 1994, Thm. 4.2 with N = 31): l = ceil(log2 d),
-// magic = ceil(2^(31+l) / d), shift = 31 + l.
-OwnerDiv make_owner_div(uint32_t d) {
-  uint32_t l = 0;
-  while ((1ull << l) < d) ++l;
-  const unsigned __int128 num = (unsigned __int128)1 << (31 + l);
-  const uint64_t magic = (uint64_t)((num + d - 1) / d);
-  return OwnerDiv{magic, 31 + l};
-}
-
 int validate_params(const moe_ep_params* p) {
   if (!p) return fail(MOE_EP_ERR_INVALID_ARG, "params is NULL");
   if (p->ep_size < 1 || p->ep_size > MOE_EP_MAX_RANKS)

@@ -44,58 +44,79 @@ struct alignas(16) TokenRec {
   int32_t t;
 };
 
-// Kernel arguments of the dispatch kernel, passed by value.
+// Kernel arguments of the dispatch kernels, passed by value.  The scalars
+// come first and contiguous, so a workgroup gets them in one batch of
+// scalar loads before it indexes the per-rank tables that follow (spread
+// over 3 KB of arguments, they had cost each workgroup a chain of dependent
+// scalar-cache round trips before its first data load).
 struct DispatchKArgs {
-  const uint8_t* hidden[kMaxRanks];    // per source rank
-  const uint8_t* scale[kMaxRanks];
-  const int32_t* ids[kMaxRanks];
-  const float* weights[kMaxRanks];
-  int32_t n[kMaxRanks];                // local_num_tokens
+  OwnerDiv div_chunks;                 // destination-major decode: / dm_chunks
+  OwnerDiv div_block_rows;             //   / dm_block_rows
+  OwnerDiv div_ep;                     //   / ep
+  OwnerDiv div_tpr;                    // receive row r / tpr
+  int32_t ep;
+  int32_t tpr;
+  int32_t top_k;
+  int32_t num_experts;
+  int32_t dm_chunks;                   // destination-major order: column chunks per row,
+  int32_t dm_block_rows;               //   rows per block on one XCD,
+  int32_t dm_blocks;                   //   blocks per XCD
+  int32_t invalid_id;
+  int32_t block;                       // threads per workgroup of the launch (blockDim.x; set by the launcher)
+  int32_t pad0;
+  uint64_t active;                     // active ranks & ((1 << ep) - 1)
+  OwnerDiv owner;
   uint8_t* ws;                         // workspace base
-  uint64_t* route;                     // [ep, tpr] destination masks (inside ws)
   int64_t part_stride;
   int64_t off_hidden, off_scale, off_ids, off_weights;
   int64_t hidden_bytes;                // H
   int64_t scale_bytes;                 // S (0 when no scales are forwarded)
-  uint64_t active;                     // active ranks & ((1 << ep) - 1)
-  OwnerDiv owner;
-  int32_t num_experts;
-  int32_t top_k;
-  int32_t ep;
-  int32_t tpr;
-  int32_t invalid_id;
-  int32_t has_weights;
-  int32_t scale_vec4;                  // scale rows copied as 4-byte words (else bytes)
-  const uint8_t* eplb[kMaxRanks];      // per source rank: its statistics row, or all NULL
-  int64_t off_eplb;
-  int64_t eplb_bytes;                  // 0 when no statistics are gathered
-  int32_t eplb_vec4;                   // statistics copied as 4-byte words (else bytes)
+  uint64_t* route;                     // [ep, tpr] destination masks (inside ws)
+  TokenRec* tokens;                    // [N] records of the real tokens (host counts only)
   const int32_t* dev_n;                // device token counts, or NULL to use n[]
   int32_t* counts;                     // [ep] counts the kernel used (read by combine)
-  TokenRec* tokens;                    // [N] records of the real tokens (host counts only)
-  int32_t token_start[kMaxRanks];      // prefix sums of n[] (host counts only)
+  int32_t has_weights;
+  int32_t scale_vec4;                  // scale rows copied as 4-byte words (else bytes)
   int32_t order;                       // MOE_EP_ORDER_SOURCE_ROW or MOE_EP_ORDER_DESTINATION
-  // Destination-major order: rows per block on one XCD, blocks per XCD,
-  // column chunks per row, and the number of (destination, row, chunk) items.
-  int32_t dm_block_rows;
-  int32_t dm_blocks;
-  int32_t dm_chunks;
-  int64_t dm_items;
   int32_t dm_u;                        // vectors per thread (7 or 8) and threads per workgroup
   int32_t dm_threads;
+  int32_t eplb_vec4;                   // statistics copied as 4-byte words (else bytes)
+  int64_t dm_items;                    // (destination, row, chunk) items
+  int64_t off_eplb;
+  int64_t eplb_bytes;                  // 0 when no statistics are gathered
+  // per source rank
+  const uint8_t* hidden[kMaxRanks];
+  const int32_t* ids[kMaxRanks];
+  const float* weights[kMaxRanks];
+  int32_t n[kMaxRanks];                // local_num_tokens
+  int32_t token_start[kMaxRanks];      // prefix sums of n[] (host counts only)
+  const uint8_t* scale[kMaxRanks];
+  const uint8_t* eplb[kMaxRanks];      // its statistics row, or all NULL
 };
 
-// Kernel arguments of the combine kernel, passed by value.
+// Kernel arguments of the combine kernel, passed by value.  The fields every
+// workgroup reads before its first row load come first and contiguous, so
+// they arrive in one batch of scalar loads; the per-rank tables follow.
 struct CombineKArgs {
+  OwnerDiv chunk_div;                       // workgroup index / 8 / chunks
+  int32_t ntok;                             // token slots (slots past it store nothing)
+  int32_t chunks;                           // column chunks of a row per token in the grid
+  int32_t block;                            // threads per workgroup (blockDim.x)
+  int32_t tpr;
+  const TokenRec* tokens;                   // [token_start[ep]] (host-count steps)
+  int64_t hidden;                           // elements per row
+  // When every read rank's expert_output lies at eo_base + d * eo_stride (the
+  // library's own combine buffers always do), row addresses are computed
+  // from these instead of loaded from the per-rank table.
+  const uint8_t* eo_base;
+  int64_t eo_stride;
+  const uint64_t* route;                    // [ep, tpr]
+  const int32_t* dev_counts;                // counts written by dispatch (device-count steps), else NULL
+  OwnerDiv tpr_div;                         // slot / tpr (device-count steps)
+  int32_t ep;
   const uint8_t* expert_output[kMaxRanks];  // per rank d: [ep*tpr, hidden]
   uint8_t* output[kMaxRanks];               // per source rank s: [n_s, hidden]
   int32_t token_start[kMaxRanks + 1];       // prefix sums of n_s (host counts)
-  const uint64_t* route;                    // [ep, tpr]
-  const TokenRec* tokens;                   // [token_start[ep]] (host-count steps)
-  const int32_t* dev_counts;                // counts written by dispatch, or NULL to use tokens
-  int64_t hidden;                           // elements per row
-  int32_t tpr;
-  int32_t ep;
 };
 
 // Launch configurations, chosen by timing variants on MI355X in the same
@@ -109,9 +130,13 @@ struct CombineKArgs {
 //    and staggered orders, blocked lane maps or several rows per workgroup
 //    were 2-10% slower.  Destination-major workgroups of one wave, 4 waves
 //    or 7 waves were 7-58% slower than 2.
-//  - combine: one column vector per thread, a whole row per workgroup (up to
-//    1024 threads), all (up to 8) destination rows loaded in one batch: 5%
-//    faster than 2 vectors x 4 rows per batch.
+//  - combine: one column vector per thread, workgroups of one or two waves
+//    over column chunks of a row, the chunks of one token on one XCD, all
+//    (up to 8) destination rows loaded in one batch.  On the DeepSeek-V3
+//    round the XCD placement made the small tiles 5% faster than a whole
+//    row per 896-thread workgroup; the same tiles placed round-robin over
+//    the XCDs were no faster than it.  One batch of 8 rows was 5% faster
+//    than 2 vectors x 4 rows per batch.
 //  - nontemporal loads and stores in both (the cache policies are in the
 //    kernels): cached combine loads were ~40% slower, and sc1 or default
 //    dispatch stores ~45% slower.
@@ -119,17 +144,17 @@ struct CombineKArgs {
 //  slower for both kernels, and a grid-stride loop alone cost combine 15%
 //  (its route-mask load became a vector load).
 constexpr int kMaxBlock = 512;           // dispatch workgroups (launch bound)
-constexpr int kMaxCombineBlock = 1024;   // combine workgroups: one whole row (launch bound)
+constexpr int kMaxCombineBlock = 128;    // combine workgroups (launch bound)
 constexpr int64_t kMaxGridY = 65535;     // chunks beyond this are looped over inside a workgroup
+constexpr int64_t kMaxCombineGrid = 1 << 24;     // combine workgroups; beyond, chunks loop
 constexpr int kDispatchBlock = 128;      // dispatch threads per workgroup, at most
 constexpr int kCombineU = 1;             // combine: vectors per thread
 constexpr int kCombineDB = 8;            // combine: destination rows loaded per batch
-constexpr int kCombineBlock = 1024;      // combine threads per workgroup, at most
-constexpr int kCombineSmallBatchMaxBlock = 512;   // combine: half batches for low fan-out up to this
+constexpr int kCombineBlock = 128;       // combine threads per workgroup, at most
 
 struct LaunchShape {
-  int grid_x;   // rows (dispatch) or real tokens (combine)
-  int grid_y;   // column chunks of a row
+  int grid_x;   // dispatch: rows; combine: workgroups (token slots rounded up to 8, x chunks)
+  int grid_y;   // column chunks of a row (combine: per token, in the 1-D grid)
   int block;    // threads per workgroup
   int u;        // vectors per thread
 };
@@ -146,6 +171,12 @@ hipError_t launch_dispatch(const DispatchKArgs& a, int vec_bytes, hipStream_t st
 // Enqueue one combine kernel over a.token_start[ep] tokens.  vec_elems must
 // divide the hidden size and every row pointer's alignment in elements.
 hipError_t launch_combine(const CombineKArgs& a, int dtype, int vec_elems, hipStream_t stream);
+
+// Multiply-shift constants for x / d with 0 <= x < 2^31 (host code).
+OwnerDiv make_owner_div(uint32_t d);
+
+// Whether the non-NULL entries of p[0..n) lie at *base + d * *stride (host code).
+bool common_stride(const uint8_t* const* p, int n, const uint8_t** base, int64_t* stride);
 
 // Launch shapes the two launchers use (host code, moe_ep_plan.cpp).
 LaunchShape row_tile(int64_t rows, int64_t nv);

@@ -50,6 +50,11 @@ template <> struct Bytes<2> { typedef uint16_t type; };
 template <> struct Bytes<1> { typedef uint8_t type; };
 
 
+// x / d for 0 <= x < 2^31, with the divisor's multiply-shift constants.
+__device__ __forceinline__ int divq(const OwnerDiv& od, int x) {
+  return (int)(((uint64_t)(uint32_t)x * od.magic) >> od.shift);
+}
+
 __device__ __forceinline__ int expert_owner(const OwnerDiv& od, uint32_t e) {
   return (int)(((uint64_t)e * od.magic) >> od.shift);
 }
@@ -103,6 +108,13 @@ __device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, int off, con
     __builtin_amdgcn_raw_buffer_store_b8(__builtin_bit_cast(W, v), r, off, 0, CP);
   }
 }
+
+// Cache policies of the row accesses (see the tuning notes with the launch
+// constants in moe_ep_internal.h).
+constexpr int kDispatchLP = kCpNt;
+constexpr int kDispatchSP = kCpNt;
+constexpr int kCombineLP = kCpNt;
+constexpr int kCombineSP = kCpNt;
 
 // ---------------------------------------------------------------------------
 // dispatch
@@ -173,6 +185,8 @@ __device__ __forceinline__ int step_count(const DispatchKArgs& a, const int s, c
 template <int VB, int U, int LP, int SP, bool DEVN>
 __device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const int r) {
   typedef typename Bytes<VB>::type V;
+  // (A division on the ALU: tpr arrives with the first batch of arguments,
+  // the multiply-shift constants would need a round trip of their own.)
   const int s = r / a.tpr;
   const int t = r - s * a.tpr;
   const int K = a.top_k;
@@ -180,24 +194,27 @@ __device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const int r
   const bool real = t < ns;
   const int32_t* __restrict__ idr = a.ids[s] + (int64_t)t * K;
   const int64_t nv = a.hidden_bytes / VB;
-  const int64_t per_block = (int64_t)blockDim.x * U;
-  const __amdgpu_buffer_rsrc_t src = row_rsrc(a.hidden[s] + (int64_t)t * a.hidden_bytes, a.hidden_bytes);
+  const int64_t per_block = (int64_t)a.block * U;
+  // A padding row (t >= n_s) has no source row: its resource has size 0, so
+  // the hardware discards its loads (they return 0 and touch no memory).
+  const __amdgpu_buffer_rsrc_t src =
+      row_rsrc(a.hidden[s] + (int64_t)t * a.hidden_bytes, real ? a.hidden_bytes : 0);
   const int64_t c_first = (int64_t)blockIdx.y * per_block;
 
   // The first chunk of the token's hidden row is loaded before the routing
   // is known, so its latency overlaps that of the expert ids.  Lanes past
-  // the end of the row load column 0 (in bounds) and store nothing.
+  // the end of the row load column 0 and store nothing.  The loads are
+  // unconditional: behind a branch, the compiler waited for them at the
+  // join before the ids load (5% slower on the ragged workload).
   int off[U];
   bool live[U];
   V v[U];
-  if (real && c_first < nv) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t c = c_first + threadIdx.x + (int64_t)u * blockDim.x;
-      live[u] = c < nv;
-      off[u] = live[u] ? (int)(c * VB) : 0;
-      v[u] = buf_load<VB, LP>(src, off[u]);
-    }
+  for (int u = 0; u < U; ++u) {
+    const int64_t c = c_first + threadIdx.x + (int64_t)u * a.block;
+    live[u] = c < nv;
+    off[u] = live[u] ? (int)(c * VB) : 0;
+    v[u] = buf_load<VB, LP>(src, off[u]);
   }
 
   const uint64_t m = route_token(a, idr, real);
@@ -210,7 +227,7 @@ __device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const int r
     // ids / weights slot of row r on every rank.
     const float* __restrict__ wr = a.has_weights ? a.weights[s] + (int64_t)t * K : nullptr;
     const int slots = a.ep * K;
-    for (int i = threadIdx.x; i < slots; i += blockDim.x) {
+    for (int i = threadIdx.x; i < slots; i += a.block) {
       const int d = i / K;
       write_slot(a, a.ws + (int64_t)d * a.part_stride, r, i - d * K, (m >> d) & 1, idr, wr);
     }
@@ -221,7 +238,7 @@ __device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const int r
       if (a.scale_vec4) {
         const int64_t nw = S / 4;
         const uint32_t* ssrc = reinterpret_cast<const uint32_t*>(a.scale[s] + (int64_t)t * S);
-        for (int64_t c = threadIdx.x; c < nw; c += blockDim.x) {
+        for (int64_t c = threadIdx.x; c < nw; c += a.block) {
           const uint32_t x = ssrc[c];
           uint64_t mm = m;
           while (mm) {
@@ -232,7 +249,7 @@ __device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const int r
         }
       } else {
         const uint8_t* ssrc = a.scale[s] + (int64_t)t * S;
-        for (int64_t c = threadIdx.x; c < S; c += blockDim.x) {
+        for (int64_t c = threadIdx.x; c < S; c += a.block) {
           const uint8_t x = ssrc[c];
           uint64_t mm = m;
           while (mm) {
@@ -253,7 +270,7 @@ __device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const int r
     if (c0 != c_first) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int64_t c = c0 + threadIdx.x + (int64_t)u * blockDim.x;
+        const int64_t c = c0 + threadIdx.x + (int64_t)u * a.block;
         live[u] = c < nv;
         off[u] = live[u] ? (int)(c * VB) : 0;
         v[u] = buf_load<VB, LP>(src, off[u]);
@@ -331,15 +348,17 @@ __device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const 
   const int rows = a.ep * a.tpr;
   const int x = i & 7;
   int k = i >> 3;
-  const int chunk = k % a.dm_chunks;
-  k /= a.dm_chunks;
-  const int j = k % a.dm_block_rows;
-  k /= a.dm_block_rows;
-  const int d = k % a.ep;
-  const int q = k / a.ep;
+  int k1 = divq(a.div_chunks, k);
+  const int chunk = k - k1 * a.dm_chunks;
+  k = k1;
+  k1 = divq(a.div_block_rows, k);
+  const int j = k - k1 * a.dm_block_rows;
+  k = k1;
+  const int q = divq(a.div_ep, k);
+  const int d = k - q * a.ep;
   const int r = x + 8 * (q * a.dm_block_rows + j);
   if (r >= rows) return;
-  const int s = r / a.tpr;
+  const int s = divq(a.div_tpr, r);
   const int t = r - s * a.tpr;
   const int K = a.top_k;
   const int ns = step_count<DEVN>(a, s, t == 0 && d == 0 && chunk == 0);
@@ -347,7 +366,7 @@ __device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const 
   const int32_t* __restrict__ idr = a.ids[s] + (int64_t)t * K;
 
   const int64_t nv = a.hidden_bytes / VB;
-  const int64_t c0 = (int64_t)chunk * blockDim.x * U;
+  const int64_t c0 = (int64_t)chunk * a.block * U;
   const __amdgpu_buffer_rsrc_t src = row_rsrc(a.hidden[s] + (int64_t)t * a.hidden_bytes, a.hidden_bytes);
   int off[U];
   bool live[U];
@@ -356,7 +375,7 @@ __device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const 
   auto load_row = [&]() {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t c = c0 + threadIdx.x + (int64_t)u * blockDim.x;
+      const int64_t c = c0 + threadIdx.x + (int64_t)u * a.block;
       live[u] = c < nv;
       off[u] = live[u] ? (int)(c * VB) : 0;
       v[u] = buf_load<VB, kCpDefault>(src, off[u]);
@@ -408,22 +427,22 @@ __device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const 
     // (the compiler turns the id select into one load from either source):
     // here that measured a few percent faster than write_slot's branches,
     // which the source-row kernel keeps.
-    for (int jj = threadIdx.x; jj < K; jj += blockDim.x) {
+    for (int jj = threadIdx.x; jj < K; jj += a.block) {
       const int64_t slot = (int64_t)r * K + jj;
       reinterpret_cast<int32_t*>(part + a.off_ids)[slot] = routed ? idr[jj] : a.invalid_id;
       if (a.has_weights)
         reinterpret_cast<float*>(part + a.off_weights)[slot] = routed ? a.weights[s][(int64_t)t * K + jj] : 0.0f;
-      if (LEAN) break;                       // top_k <= 64 < blockDim.x: one pass
+      if (LEAN) break;                       // top_k <= 64 < a.block: one pass
     }
     if (!LEAN && routed && a.scale_bytes) {
       const int64_t S = a.scale_bytes;
       uint8_t* dst = part + a.off_scale + (int64_t)r * S;
       if (a.scale_vec4) {
         const uint32_t* ssrc = reinterpret_cast<const uint32_t*>(a.scale[s] + (int64_t)t * S);
-        for (int64_t c = threadIdx.x; c < S / 4; c += blockDim.x) reinterpret_cast<uint32_t*>(dst)[c] = ssrc[c];
+        for (int64_t c = threadIdx.x; c < S / 4; c += a.block) reinterpret_cast<uint32_t*>(dst)[c] = ssrc[c];
       } else {
         const uint8_t* ssrc = a.scale[s] + (int64_t)t * S;
-        for (int64_t c = threadIdx.x; c < S; c += blockDim.x) dst[c] = ssrc[c];
+        for (int64_t c = threadIdx.x; c < S; c += a.block) dst[c] = ssrc[c];
       }
     }
   }
@@ -522,18 +541,19 @@ __device__ __forceinline__ typename CVec<DT, VE>::type pack(const float (&acc)[V
   return v;
 }
 
-template <int DT, int VE, int U, int DB, int LP, int SP, bool ONEPASS, bool SMALL>
-__device__ __forceinline__ void combine_token(const CombineKArgs& a, const int b) {
+template <int DT, int VE, int U, int DB, int LP, int SP, bool ONEPASS, bool STRIDED, bool DEVN>
+__device__ __forceinline__ void combine_token(const CombineKArgs& a, const int b, const int chunk, const bool store) {
   typedef typename CVec<DT, VE>::type V;
   int s;
   int t;
   uint64_t m;
-  if (a.dev_counts) {
-    // Slots of every possible token; those past the count dispatch used hold none.
-    s = b / a.tpr;
+  if (DEVN) {
+    // Slots of every possible token (b = s*tpr + t); those past the count
+    // dispatch used hold none.
+    s = (int)(((uint64_t)b * a.tpr_div.magic) >> a.tpr_div.shift);
     t = b - s * a.tpr;
     if (t >= a.dev_counts[s]) return;
-    m = a.route[(int64_t)s * a.tpr + t];
+    m = a.route[b];
   } else {
     // Real token b's record, written by dispatch: one load instead of a
     // search over the per-source prefix followed by the mask load.
@@ -546,11 +566,11 @@ __device__ __forceinline__ void combine_token(const CombineKArgs& a, const int b
   const int64_t nv = a.hidden / VE;
   constexpr int esz = DT == MOE_EP_F32 ? 4 : 2;
   const int64_t row_bytes = a.hidden * esz;
-  const int64_t per_block = (int64_t)blockDim.x * U;
+  const int64_t per_block = (int64_t)a.block * U;
   constexpr int VB = VE * esz;
   const __amdgpu_buffer_rsrc_t out = row_rsrc(a.output[s] + (int64_t)t * row_bytes, row_bytes);
 
-  for (int64_t c0 = (int64_t)blockIdx.y * per_block; c0 < nv; c0 += (int64_t)gridDim.y * per_block) {
+  auto pass = [&](const int64_t c0) {
     // Lanes past the end of the row read column 0 (in bounds) and store
     // nothing, so every load below is unconditional and they all issue
     // before the first add waits.
@@ -558,7 +578,7 @@ __device__ __forceinline__ void combine_token(const CombineKArgs& a, const int b
     bool live[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t c = c0 + threadIdx.x + (int64_t)u * blockDim.x;
+      const int64_t c = c0 + threadIdx.x + (int64_t)u * a.block;
       live[u] = c < nv;
       off[u] = live[u] ? (int)(c * VB) : 0;
     }
@@ -581,7 +601,8 @@ __device__ __forceinline__ void combine_token(const CombineKArgs& a, const int b
         if (mm) {
           const int d = __builtin_ctzll(mm);
           mm &= mm - 1;
-          rows[k] = row_rsrc(a.expert_output[d] + r * row_bytes, row_bytes);
+          const uint8_t* eo = STRIDED ? a.eo_base + (int64_t)d * a.eo_stride : a.expert_output[d];
+          rows[k] = row_rsrc(eo + r * row_bytes, row_bytes);
           cnt = k + 1;
         } else {
           rows[k] = rows[k > 0 ? k - 1 : 0];
@@ -597,46 +618,74 @@ __device__ __forceinline__ void combine_token(const CombineKArgs& a, const int b
 #pragma unroll
         for (int u = 0; u < U; ++u) unpack_add<DT, VE>(v[k][u], acc[u], k < cnt);
     };
-    // SMALL: a token that reached at most DB/2 ranks loads only DB/2 rows
-    // (a uniform branch).  Taken for workgroups of up to 8 waves, where it
-    // measured 15% faster on a ragged round of 8 KiB rows (2.8 ranks per
-    // token) and even on a 32-rank one; with 14-wave workgroups (14 KiB
-    // rows) it was 6% slower, so those keep one batch size.
+    // A token that reached at most DB/2 ranks loads only DB/2 rows (a
+    // uniform branch): 20% faster on a ragged round of 8 KiB rows (2.8 ranks
+    // per token), even on the others.
     // A batch needs at least one row: its first slot is the one every
     // unused slot repeats.  A token that reached no rank takes no batch.
-    if (SMALL && mm != 0 && __builtin_popcountll(mm) <= DB / 2) {
+    if (mm != 0 && __builtin_popcountll(mm) <= DB / 2) {
       batch(std::integral_constant<int, DB / 2>{});
     } else {
       while (mm) batch(std::integral_constant<int, DB>{});
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (live[u]) buf_store<VB, SP>(out, off[u], pack<DT, VE>(acc[u]));
-    // The grid covers the row: no loop (its back edge measured ~2% slower).
-    if (ONEPASS) break;
+      if (store && live[u]) buf_store<VB, SP>(out, off[u], pack<DT, VE>(acc[u]));
+  };
+  if (ONEPASS) {
+    // The grid covers the row: straight-line code, no loop test between the
+    // argument loads and the row loads.
+    pass((int64_t)chunk * per_block);
+  } else {
+    for (int64_t c0 = (int64_t)chunk * per_block; c0 < nv; c0 += (int64_t)a.chunks * per_block) pass(c0);
   }
 }
 
-// Grid: x = real token (prefix over source ranks), or one of all ep*tpr
-// token slots after a dispatch that read device-resident counts; y = column
-// chunk of the row.
-template <int DT, int VE, int U, int DB, int LP, int SP, bool ONEPASS, bool SMALL>
+// Grid (1-D): one workgroup per (token slot, column chunk).  Token slots are
+// the real tokens (prefix over source ranks), or all ep*tpr slots after a
+// dispatch that read device-resident counts.  Workgroup i runs on XCD i % 8,
+// so i is decoded as: token 8q + x on XCD x = i % 8, and its chunks one after
+// another on that XCD (q and the chunk from i / 8).  Placing all chunks of a
+// token on one XCD made these small workgroups 5% faster on the
+// DeepSeek-V3-shaped round than one 896-thread workgroup per token; placed
+// round-robin they were no faster.
+template <int DT, int VE, int U, int DB, int LP, int SP, bool ONEPASS, bool STRIDED, bool DEVN>
 __global__ void __launch_bounds__(kMaxCombineBlock)
 combine_kernel(const CombineKArgs a) {
-  // One workgroup per token slot, no grid-stride loop: with stores ahead of
-  // it in the same workgroup the token-record load could not be a scalar load.
-  combine_token<DT, VE, U, DB, LP, SP, ONEPASS, SMALL>(a, blockIdx.x);
+  // One workgroup per item, no grid-stride loop: with stores ahead of it in
+  // the same workgroup the token-record load could not be a scalar load.
+  // Every test or argument load between the start and the first row load
+  // costs the workgroup another dependent round trip, hence: i / 8 / chunks
+  // is a multiply and a shift on arguments that arrive in the first batch,
+  // the block size comes with them, DEVN (device-resident counts) and
+  // STRIDED are instantiations, and a slot past the last token (the grid
+  // holds whole groups of 8) repeats the last token's loads and stores
+  // nothing instead of returning.
+  const int i = blockIdx.x;
+  const int rest = i >> 3;
+  const int q = (int)(((uint64_t)rest * a.chunk_div.magic) >> a.chunk_div.shift);
+  const int chunk = rest - q * a.chunks;
+  const int b = q * 8 + (i & 7);
+  const bool real = b < a.ntok;
+  combine_token<DT, VE, U, DB, LP, SP, ONEPASS, STRIDED, DEVN>(a, real ? b : a.ntok - 1, chunk, real);
+}
+
+template <int DT, int VE>
+const void* pick_combine(bool onepass, bool strided, bool devn) {
+#define MOE_EP_CK(OP, ST, DV) \
+  reinterpret_cast<const void*>(&combine_kernel<DT, VE, kCombineU, kCombineDB, kCombineLP, kCombineSP, OP, ST, DV>)
+  if (onepass) {
+    if (strided) return devn ? MOE_EP_CK(true, true, true) : MOE_EP_CK(true, true, false);
+    return devn ? MOE_EP_CK(true, false, true) : MOE_EP_CK(true, false, false);
+  }
+  if (strided) return devn ? MOE_EP_CK(false, true, true) : MOE_EP_CK(false, true, false);
+  return devn ? MOE_EP_CK(false, false, true) : MOE_EP_CK(false, false, false);
+#undef MOE_EP_CK
 }
 
 
 }  // namespace
 
-// Cache policies of the row accesses (see the tuning notes with the launch
-// constants in moe_ep_internal.h).
-constexpr int kDispatchLP = kCpNt;
-constexpr int kDispatchSP = kCpNt;
-constexpr int kCombineLP = kCpNt;
-constexpr int kCombineSP = kCpNt;
 
 // Kernel for a vector width, a tile width (4, 7 or 8 vectors per thread) and a
 // count source, as a table: (VB, U, DEVN) are template arguments.
@@ -664,7 +713,14 @@ template <int VB, int U, bool DEVN> struct DestinationLeanKernel {
   static const void* fn() { return reinterpret_cast<const void*>(&dispatch_dst_kernel<VB, U, kDispatchSP, DEVN, true>); }
 };
 
-hipError_t launch_dispatch(const DispatchKArgs& a, int vec_bytes, hipStream_t stream) {
+hipError_t launch_dispatch(const DispatchKArgs& args, int vec_bytes, hipStream_t stream) {
+  DispatchKArgs a = args;
+  a.div_tpr = make_owner_div((uint32_t)std::max(1, a.tpr));
+  if (a.order == MOE_EP_ORDER_DESTINATION) {
+    a.div_chunks = make_owner_div((uint32_t)std::max(1, a.dm_chunks));
+    a.div_block_rows = make_owner_div((uint32_t)std::max(1, a.dm_block_rows));
+    a.div_ep = make_owner_div((uint32_t)std::max(1, a.ep));
+  }
   const int64_t extra = a.eplb_bytes ? a.ep : 0;
   const bool devn = a.dev_n != nullptr;
   const void* fn;
@@ -677,28 +733,35 @@ hipError_t launch_dispatch(const DispatchKArgs& a, int vec_bytes, hipStream_t st
               : pick_kernel<DestinationKernel>(vec_bytes, a.dm_u, devn);
     grid = dim3((unsigned)(a.dm_items + extra));
     block = dim3(a.dm_threads);
+    a.block = a.dm_threads;
   } else {
     const LaunchShape sh = dispatch_shape((int64_t)a.ep * a.tpr + extra, a.hidden_bytes, vec_bytes);
     if (sh.grid_x <= 0) return hipSuccess;
     fn = pick_kernel<SourceRowKernel>(vec_bytes, sh.u, devn);
     grid = dim3(sh.grid_x, sh.grid_y);
     block = dim3(sh.block);
+    a.block = sh.block;
   }
   if (!fn) return hipErrorInvalidValue;
-  void* args[] = {const_cast<DispatchKArgs*>(&a)};
-  return hipLaunchKernel(fn, grid, block, args, 0, stream);
+  void* kargs[] = {&a};
+  return hipLaunchKernel(fn, grid, block, kargs, 0, stream);
 }
 
-hipError_t launch_combine(const CombineKArgs& a, int dtype, int vec_elems, hipStream_t stream) {
-  const LaunchShape sh = combine_shape(a.dev_counts ? (int64_t)a.ep * a.tpr : a.token_start[a.ep], a.hidden, vec_elems);
+hipError_t launch_combine(const CombineKArgs& args, int dtype, int vec_elems, hipStream_t stream) {
+  CombineKArgs a = args;
+  a.ntok = a.dev_counts ? a.ep * a.tpr : a.token_start[a.ep];
+  const LaunchShape sh = combine_shape(a.ntok, a.hidden, vec_elems);
   if (sh.grid_x <= 0) return hipSuccess;
+  a.chunks = sh.grid_y;
   const void* fn = nullptr;
   const bool onepass = (int64_t)sh.grid_y * sh.block * kCombineU >= a.hidden / vec_elems;
-  const bool small = sh.block <= kCombineSmallBatchMaxBlock;
-#define MOE_EP_CK(DT, VE, OP, SM) reinterpret_cast<const void*>(&combine_kernel<DT, VE, kCombineU, kCombineDB, kCombineLP, kCombineSP, OP, SM>)
+  const bool strided = common_stride(a.expert_output, a.ep, &a.eo_base, &a.eo_stride);
+  const bool devn = a.dev_counts != nullptr;
+  a.block = sh.block;
+  a.chunk_div = make_owner_div((uint32_t)a.chunks);
+  if (devn) a.tpr_div = make_owner_div((uint32_t)a.tpr);
 #define MOE_EP_C(DT, VE) \
-    case VE: fn = onepass ? (small ? MOE_EP_CK(DT, VE, true, true) : MOE_EP_CK(DT, VE, true, false)) \
-                          : (small ? MOE_EP_CK(DT, VE, false, true) : MOE_EP_CK(DT, VE, false, false)); break;
+    case VE: fn = pick_combine<DT, VE>(onepass, strided, devn); break;
   if (dtype == MOE_EP_F32) {
     switch (vec_elems) {
       MOE_EP_C(MOE_EP_F32, 4) MOE_EP_C(MOE_EP_F32, 2) MOE_EP_C(MOE_EP_F32, 1)
@@ -718,9 +781,8 @@ hipError_t launch_combine(const CombineKArgs& a, int dtype, int vec_elems, hipSt
     return hipErrorInvalidValue;
   }
 #undef MOE_EP_C
-#undef MOE_EP_CK
-  void* args[] = {const_cast<CombineKArgs*>(&a)};
-  return hipLaunchKernel(fn, dim3(sh.grid_x, sh.grid_y), dim3(sh.block), args, 0, stream);
+  void* kargs[] = {&a};
+  return hipLaunchKernel(fn, dim3(sh.grid_x), dim3(sh.block), kargs, 0, stream);
 }
 
 }  // namespace moe_ep_detail

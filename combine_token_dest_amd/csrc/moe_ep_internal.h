@@ -130,13 +130,14 @@ struct CombineKArgs {
 //    and staggered orders, blocked lane maps or several rows per workgroup
 //    were 2-10% slower.  Destination-major workgroups of one wave, 4 waves
 //    or 7 waves were 7-58% slower than 2.
-//  - combine: one column vector per thread, workgroups of one or two waves
-//    over column chunks of a row, the chunks of one token on one XCD, all
-//    (up to 8) destination rows loaded in one batch.  On the DeepSeek-V3
-//    round the XCD placement made the small tiles 5% faster than a whole
-//    row per 896-thread workgroup; the same tiles placed round-robin over
-//    the XCDs were no faster than it.  One batch of 8 rows was 5% faster
-//    than 2 vectors x 4 rows per batch.
+//  - combine: one column vector per thread, one-wave workgroups over
+//    column chunks of a row, the chunks of one token on one XCD, all (up
+//    to 8) destination rows loaded in one batch.  On the DeepSeek-V3 round
+//    the XCD placement made the small tiles faster than a whole row per
+//    896-thread workgroup; the same tiles placed round-robin over the XCDs
+//    were no faster than it.  One wave beat two by 1% there and 2.4% on a
+//    32-rank round of 8 KiB rows (0.4% behind on a 16-rank fp8 round).
+//    One batch of 8 rows was 5% faster than 2 vectors x 4 rows per batch.
 //  - nontemporal loads and stores in both (the cache policies are in the
 //    kernels): cached combine loads were ~40% slower, and sc1 or default
 //    dispatch stores ~45% slower.
@@ -144,13 +145,13 @@ struct CombineKArgs {
 //  slower for both kernels, and a grid-stride loop alone cost combine 15%
 //  (its route-mask load became a vector load).
 constexpr int kMaxBlock = 512;           // dispatch workgroups (launch bound)
-constexpr int kMaxCombineBlock = 128;    // combine workgroups (launch bound)
+constexpr int kMaxCombineBlock = 64;     // combine workgroups (launch bound)
 constexpr int64_t kMaxGridY = 65535;     // chunks beyond this are looped over inside a workgroup
 constexpr int64_t kMaxCombineGrid = 1 << 24;     // combine workgroups; beyond, chunks loop
 constexpr int kDispatchBlock = 128;      // dispatch threads per workgroup, at most
 constexpr int kCombineU = 1;             // combine: vectors per thread
 constexpr int kCombineDB = 8;            // combine: destination rows loaded per batch
-constexpr int kCombineBlock = 128;       // combine threads per workgroup, at most
+constexpr int kCombineBlock = 64;        // combine threads per workgroup, at most
 
 struct LaunchShape {
   int grid_x;   // dispatch: rows; combine: workgroups (token slots rounded up to 8, x chunks)

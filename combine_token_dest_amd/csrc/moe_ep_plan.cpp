@@ -117,26 +117,28 @@ bool common_stride(const uint8_t* const* p, int n, const uint8_t** base, int64_t
 
 // Destination-major order: rows per XCD block such that a block's source
 // rows (about 512 KiB) stay in the XCD's L2 while every destination re-reads
-// them.  It launches one workgroup per (destination, row), each of which
-// routes its token before storing; that only pays off when the grid holds at
-// least two resident generations of workgroups, so one generation's routing
-// overlaps another's stores, and while the source-row grid alone (one
-// routing per row) does not fill the chip.  AUTO takes it then, for groups
-// of at most 16 ranks and ep * ep * tpr <= 16384, and the source-row order
-// otherwise.  Measured with 14 KiB rows (three interleaved runs each):
-//   8 ranks: destination-major 3.6% faster at 128 tokens per rank and 9% at
-//   256 (two and four generations), 5.6% and 8.6% slower at 32 and 64 (half
-//   and one), even at 16 or fewer;
-//   4 ranks: 8.6% faster at 512 tokens, 4% slower at 256 (one generation)
-//   and 4.4% slower at 1024 (4096 source rows fill the chip);
-//   16 ranks: 4.6% and 10% faster at 32 and 64 tokens, even at 16.
-// With 16 ranks and 256 tokens, 32 ranks, or 512-token ragged steps, it was
+// them.  It launches one workgroup per (destination, row); AUTO takes it for
+// groups of at most 16 ranks with ep * ep * tpr <= 16384 while the
+// source-row grid alone (one workgroup per row) does not fill the chip, and
+// the source-row order otherwise.  Measured with the current kernels (µs
+// per dispatch, source-row vs destination-major, one box):
+//   14 KiB rows, 8 ranks: 1 token per rank 5.10 vs 4.34, 4: 5.58 vs 4.47,
+//   16: 5.96 vs 5.09, 32: 7.18 vs 6.63, 64: 10.62 vs 10.44, 128: 18.58 vs
+//   16.75, 256: 36.76 vs 36.04;  4 ranks: 16: 5.35 vs 4.51, 64: 6.19 vs
+//   5.38, 256: 13.58 vs 12.48, 512: 26.76 vs 23.99, 1024 (4096 source rows
+//   fill the chip): 53.56 vs 55.54;  16 ranks: 4: 6.16 vs 4.82, 16: 8.40 vs
+//   7.66, 64: 23.01 vs 20.51;
+//   8 KiB rows: 8 ranks x 32/64/128 and 16 x 32/64 tokens 2-10% faster,
+//   4 x 256 even, 4 x 1024 (chip filled) 11% slower; 512-byte rows (4 and
+//   8 ranks x 16 tokens) 9-13% faster.
+// With 16 ranks and 256 tokens, 32 ranks, or 512-token ragged steps it was
 // 1.2-2x slower (most of its workgroups copy nothing when a row reaches few
-// of many ranks).
+// of many ranks).  An earlier version of this kernel, whose workgroups
+// waited on a longer chain of argument loads, also needed two resident
+// generations of workgroups to win.
 constexpr int64_t kDmBlockBytes = 512 * 1024;
 constexpr int64_t kDmAutoMaxPairs = 16384;   // ep * ep * tpr
 constexpr int kDmAutoMaxRanks = 16;
-constexpr int64_t kDmAutoMinGenerations = 2;
 
 bool plan_dispatch(DispatchKArgs& a, int vec_bytes, int requested) {
   const int64_t rows = (int64_t)a.ep * a.tpr;
@@ -157,8 +159,6 @@ bool plan_dispatch(DispatchKArgs& a, int vec_bytes, int requested) {
   if (est + a.ep > 2147483647.0) return automatic;     // AUTO falls back to the source-row order
   const int64_t items = 8 * nq * a.ep * b * chunks;
   if (automatic) {
-    const int64_t resident = kResidentWaves / ((tile.block + 63) / 64);   // workgroups on the chip at once
-    if (items < kDmAutoMinGenerations * resident) return true;
     const LaunchShape src = dispatch_shape(rows, a.hidden_bytes, vec_bytes);
     if (rows >= kResidentWaves / ((src.block + 63) / 64)) return true;    // the source-row grid fills the chip
   }

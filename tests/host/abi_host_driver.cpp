@@ -86,27 +86,28 @@ int main() {
   }
 
   // The copy order AUTO picks: destination-major for groups of at most 16
-  // ranks, ep * ep * tpr <= 16384, at least two resident generations of
-  // (destination, row) workgroups and fewer source rows than fill the chip;
-  // else source-row.
+  // ranks with ep * ep * tpr <= 16384 while the source rows alone do not
+  // fill the chip; else source-row.
   struct OrderCase { int ep, tpr; int64_t row_bytes; int requested, expect; };
   const OrderCase order_cases[] = {
       {8, 128, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION},    // DeepSeek-V3 decode round
       {8, 256, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION},
-      {8, 64, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},      // one generation
-      {8, 32, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},
-      {8, 1, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},
+      {8, 64, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION},
+      {8, 32, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION},
+      {8, 1, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION},
       {8, 512, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},     // ep * ep * tpr > 16384
-      {8, 128, 8192, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},      // one-wave tiles: one generation
+      {8, 128, 8192, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION},
       {4, 512, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION},
-      {4, 256, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},     // one generation
+      {4, 256, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION},
       {4, 1024, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},    // 4096 source rows fill the chip
+      {4, 1024, 8192, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},     // 4096 two-wave source rows too
+      {2, 2048, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},
       {16, 32, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION},
       {16, 64, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION},
-      {16, 16, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},
+      {16, 16, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION},
       {16, 256, 7168, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},     // 16-rank fp8 round
       {32, 256, 8192, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},     // more than 16 ranks
-      {4, 16, 512, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW},
+      {4, 16, 512, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION},
       {4, 16, 512, MOE_EP_ORDER_DESTINATION, MOE_EP_ORDER_DESTINATION},
       {8, 0, 14336, MOE_EP_ORDER_DESTINATION, MOE_EP_ORDER_DESTINATION},
       {8, 128, 14336, MOE_EP_ORDER_SOURCE_ROW, MOE_EP_ORDER_SOURCE_ROW},

@@ -78,12 +78,12 @@ def test_f16_combine_dsv3_shape(order):
     parity.run_step(c, zero_copy=order == "destination", order=order)
 
 
-@pytest.mark.parametrize("name,expect", [("tiny", "source"), ("dsv3", "destination"),
+@pytest.mark.parametrize("name,expect", [("tiny", "destination"), ("dsv3", "destination"),
                                          ("fp8", "source"), ("ragged", "source")])
 def test_auto_order_choice(name, expect):
     """AUTO takes the destination-major kernel only for groups of at most 16
-    ranks with ep^2 * tokens_per_rank <= 16384 whose (destination, row)
-    workgroups fill the chip at least twice, and stays bit-exact."""
+    ranks with ep^2 * tokens_per_rank <= 16384 whose source rows alone do
+    not fill the chip, and stays bit-exact."""
     w = wl.BY_NAME[name]
     log(f"[parity] workload {name} auto order")
     c = parity.case_from_workload(w)

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstring>
 #include <initializer_list>
+#include <vector>
 
 #include "moe_ep.h"
 #include "moe_ep_internal.h"
@@ -128,6 +129,60 @@ int main() {
     } else {
       expect(k.dm_items == 0, "no destination-major items");
     }
+  }
+
+  // Multiply-shift division (item decodes): exact for 0 <= x < 2^31.
+  for (uint32_t dv : {1u, 2u, 3u, 5u, 7u, 8u, 14u, 16u, 36u, 64u, 127u, 128u, 1000u, 65535u, 65536u,
+                      (1u << 30) + 7u, 0x7fffffffu}) {
+    const moe_ep_detail::OwnerDiv od = moe_ep_detail::make_owner_div(dv);
+    for (uint64_t x : {(uint64_t)0, (uint64_t)1, (uint64_t)dv - 1, (uint64_t)dv, (uint64_t)dv + 1,
+                       (uint64_t)12345, (uint64_t)1 << 20, ((uint64_t)1 << 31) - 2, ((uint64_t)1 << 31) - 1}) {
+      if (x >= ((uint64_t)1 << 31)) continue;
+      expect(((x * od.magic) >> od.shift) == x / dv, "multiply-shift division");
+    }
+  }
+
+  // Combine grid: every (token slot, chunk) once, token 8q + x on XCD x.
+  for (int64_t tokens : {1, 7, 8, 9, 1000, 1024}) {
+    const LaunchShape c = moe_ep_detail::combine_shape(tokens, 7168, 8);
+    const int64_t slots = (tokens + 7) / 8 * 8;
+    expect(c.grid_x == slots * c.grid_y && c.block == moe_ep_detail::kCombineBlock, "combine grid");
+    expect((int64_t)c.grid_y * c.block >= 7168 / 8, "combine chunks cover the row");
+    const moe_ep_detail::OwnerDiv od = moe_ep_detail::make_owner_div((uint32_t)c.grid_y);
+    std::vector<int> seen((size_t)slots * c.grid_y, 0);
+    for (int64_t i = 0; i < c.grid_x; ++i) {
+      const int64_t rest = i >> 3;
+      const int64_t q = (int64_t)(((uint64_t)rest * od.magic) >> od.shift);
+      const int64_t chunk = rest - q * c.grid_y;
+      const int64_t b = q * 8 + (i & 7);
+      expect(b % 8 == i % 8 && chunk >= 0 && chunk < c.grid_y && b < slots, "combine decode");
+      if (b < slots && chunk >= 0 && chunk < c.grid_y) ++seen[(size_t)(b * c.grid_y + chunk)];
+    }
+    for (int v : seen) expect(v == 1, "combine decode covers every item once");
+  }
+
+  // Constant-stride detection of the combine inputs (NULL = masked rank).
+  {
+    using moe_ep_detail::common_stride;
+    const uint8_t* base = nullptr;
+    int64_t stride = -1;
+    uint8_t* const b0 = reinterpret_cast<uint8_t*>(uintptr_t(1) << 36);
+    const uint8_t* p4[4] = {b0, b0 + 1000, b0 + 2000, b0 + 3000};
+    expect(common_stride(p4, 4, &base, &stride) && base == b0 && stride == 1000, "stride forward");
+    const uint8_t* r4[4] = {b0 + 3000, b0 + 2000, b0 + 1000, b0};
+    expect(common_stride(r4, 4, &base, &stride) && base == b0 + 3000 && stride == -1000, "stride reverse");
+    const uint8_t* g4[4] = {nullptr, b0 + 1000, nullptr, b0 + 3000};
+    expect(common_stride(g4, 4, &base, &stride) && base == b0 && stride == 1000, "stride with masked ranks");
+    const uint8_t* u4[4] = {b0, b0 + 1000, b0 + 2001, b0 + 3000};
+    expect(!common_stride(u4, 4, &base, &stride), "uneven");
+    const uint8_t* h4[4] = {nullptr, b0 + 1000, nullptr, b0 + 2001};
+    expect(!common_stride(h4, 4, &base, &stride), "stride not a whole multiple across a gap");
+    const uint8_t* one[3] = {nullptr, b0 + 77, nullptr};
+    expect(common_stride(one, 3, &base, &stride) && base == b0 + 77 && stride == 0, "one rank");
+    const uint8_t* none[2] = {nullptr, nullptr};
+    expect(common_stride(none, 2, &base, &stride) && base == nullptr && stride == 0, "no rank");
+    const uint8_t* same[3] = {b0, b0, b0};
+    expect(common_stride(same, 3, &base, &stride) && base == b0 && stride == 0, "one buffer for every rank");
   }
 
   // Validation paths of one handle over a fake workspace.

@@ -485,6 +485,63 @@ def test_masked_rank_buffers_never_read():
     moe.destroy()
 
 
+@pytest.mark.parametrize("layout", ["forward", "reverse", "uneven", "misaligned", "misaligned_uneven", "masked", "mixed"])
+def test_combine_input_layouts(layout):
+    """Combine inputs placed in one buffer in different layouts.  The kernel
+    computes row addresses from a base and a stride when the read ranks'
+    inputs lie at a constant stride (forward, reverse, masked: the masked
+    ranks are never read, so their inputs do not count) and reads the
+    per-rank table otherwise (uneven; mixed: some ranks pass their combine
+    input buffer).  The misaligned layouts (2-byte alignment only, so one
+    element per lane) take each path once."""
+    log(f"[parity] combine input layout {layout}")
+    if layout == "masked":
+        w = wl.BY_NAME["ragged"]
+        c = parity.case_from_workload(w, local_num_tokens=[50, 0, 31, 7, 0, 0, 64, 9])
+    else:
+        w = dataclasses.replace(wl.BY_NAME["dsv3"], max_tokens_per_rank=16)
+        c = parity.case_from_workload(w)
+    p = parity.oracle_params(c)
+    om = oracle.OracleMoEEp(p)
+    ores = om.dispatch(c.hidden, c.ids, c.weights, runtime_max_tokens_per_rank=c.rtpr, active_rank_mask=c.mask)
+    eo_host = parity.combine_inputs_host(c, ores)
+    oout = om.combine(eo_host, c.combine_dtype, active_rank_mask=c.mask)
+    moe = parity.make_gpu(c)
+    hid, ids, wt, _ = parity.upload(c)
+    moe.dispatch(hid, ids, wt, runtime_max_tokens_per_rank=c.rtpr, active_rank_mask=c.mask)
+    n = eo_host[0].size                        # elements per rank
+    ep = c.ep
+    gap = 4096                                 # elements between consecutive inputs
+    if layout in ("forward", "masked", "mixed"):
+        offs = [d * (n + gap) for d in range(ep)]
+    elif layout == "reverse":
+        offs = [(ep - 1 - d) * (n + gap) for d in range(ep)]
+    elif layout == "uneven":
+        offs, o = [], 0
+        for d in range(ep):
+            offs.append(o)
+            o += n + gap + 64 * d * d
+    elif layout == "misaligned":               # odd element offsets at a constant stride
+        offs = [d * (n + gap) + 1 for d in range(ep)]
+    else:                                      # misaligned_uneven
+        offs = [d * (n + gap) + 1 + (d % 3) for d in range(ep)]
+    big = torch.full((max(offs) + n + 8,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    eo = []
+    for d in range(ep):
+        v = big[offs[d]:offs[d] + n].view(eo_host[d].shape)
+        v.copy_(parity.host_to_torch(eo_host[d], c.combine_dtype).view(eo_host[d].shape))
+        eo.append(v)
+    if layout == "mixed":
+        for d in (2, 5):
+            buf = moe.get_combine_input_buffer(d, torch.bfloat16)
+            buf.copy_(eo[d].view(buf.shape))
+            eo[d] = None
+    gout = moe.combine(eo, active_rank_mask=c.mask)
+    torch.cuda.synchronize()
+    parity.compare_combine(c, gout, oout, f"layout {layout}")
+    moe.destroy()
+
+
 # --------------------------------------------------------------------------
 # Call protocol on the GPU path
 # --------------------------------------------------------------------------

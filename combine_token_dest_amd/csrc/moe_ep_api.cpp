@@ -487,7 +487,7 @@ int moe_ep_dispatch(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispa
   uint64_t scale_align_or = has_s ? (uint64_t)p.scale_row_bytes : 0;
   for (int s = 0; s < ep; ++s) {
     const int32_t n = host_n[s];
-    k.n[s] = n;
+    k.src[s].n = n;
     if (n == 0) continue;
     if (!a->hidden[s] || !a->topk_ids[s])
       return fail(MOE_EP_ERR_INVALID_ARG, "rank %d: NULL hidden or topk_ids with %d tokens", s, n);
@@ -502,10 +502,10 @@ int moe_ep_dispatch(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispa
       scale_align_or |= reinterpret_cast<uintptr_t>(a->hidden_scale[s]);
     }
     hidden_align_or |= reinterpret_cast<uintptr_t>(a->hidden[s]);
-    k.hidden[s] = static_cast<const uint8_t*>(a->hidden[s]);
-    k.ids[s] = a->topk_ids[s];
-    k.weights[s] = has_w ? a->topk_weights[s] : nullptr;
-    k.scale[s] = has_s ? static_cast<const uint8_t*>(a->hidden_scale[s]) : nullptr;
+    k.src[s].hidden = static_cast<const uint8_t*>(a->hidden[s]);
+    k.src[s].ids = a->topk_ids[s];
+    k.src[s].weights = has_w ? a->topk_weights[s] : nullptr;
+    k.src[s].scale = has_s ? static_cast<const uint8_t*>(a->hidden_scale[s]) : nullptr;
   }
   const int vec_bytes = (int)pow2_divisor(hidden_align_or, 16);
   uint64_t eplb_align_or = (uint64_t)p.eplb_stats_bytes;
@@ -513,14 +513,14 @@ int moe_ep_dispatch(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispa
     for (int s = 0; s < ep; ++s) {
       if (!a->eplb_local_stats[s]) return fail(MOE_EP_ERR_INVALID_ARG, "rank %d: NULL eplb_local_stats", s);
       eplb_align_or |= reinterpret_cast<uintptr_t>(a->eplb_local_stats[s]);
-      k.eplb[s] = static_cast<const uint8_t*>(a->eplb_local_stats[s]);
+      k.src[s].eplb = static_cast<const uint8_t*>(a->eplb_local_stats[s]);
     }
   }
   k.dev_n = a->local_num_tokens_device;
   k.counts = reinterpret_cast<int32_t*>(h->ws + h->L.off_counts);
   k.tokens = reinterpret_cast<TokenRec*>(h->ws + h->L.off_tokens);
   for (int s = 0, start = 0; s < ep; ++s) {
-    k.token_start[s] = start;
+    k.src[s].token_start = start;
     start += host_n[s];
   }
   k.off_eplb = h->L.off_eplb;

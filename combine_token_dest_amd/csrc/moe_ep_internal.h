@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime_api.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "moe_ep.h"
@@ -44,6 +45,21 @@ struct alignas(16) TokenRec {
   int32_t t;
 };
 
+// What the dispatch kernels read of one source rank: one 64-byte record, so
+// a workgroup gets all of it with one scalar load (in separate per-field
+// tables it took two dependent round trips to four cache lines).
+struct SourceRank {
+  const uint8_t* hidden;               // [n, hidden_row_bytes]
+  const int32_t* ids;                  // [n, top_k]
+  const float* weights;                // [n, top_k], or NULL
+  const uint8_t* scale;                // [n, scale_row_bytes], or NULL
+  const uint8_t* eplb;                 // its statistics row, or NULL
+  int32_t n;                           // local_num_tokens
+  int32_t token_start;                 // prefix sum of n over the ranks before (host counts only)
+  int64_t pad[2];
+};
+static_assert(sizeof(SourceRank) == 64, "one cache line per source rank");
+
 // Kernel arguments of the dispatch kernels, passed by value.  The scalars
 // come first and contiguous, so a workgroup gets them in one batch of
 // scalar loads before it indexes the per-rank tables that follow (spread
@@ -84,15 +100,10 @@ struct DispatchKArgs {
   int64_t dm_items;                    // (destination, row, chunk) items
   int64_t off_eplb;
   int64_t eplb_bytes;                  // 0 when no statistics are gathered
-  // per source rank
-  const uint8_t* hidden[kMaxRanks];
-  const int32_t* ids[kMaxRanks];
-  const float* weights[kMaxRanks];
-  int32_t n[kMaxRanks];                // local_num_tokens
-  int32_t token_start[kMaxRanks];      // prefix sums of n[] (host counts only)
-  const uint8_t* scale[kMaxRanks];
-  const uint8_t* eplb[kMaxRanks];      // its statistics row, or all NULL
+  int64_t pad1[6];                     // the per-rank records start on a 64-byte boundary
+  SourceRank src[kMaxRanks];           // per source rank
 };
+static_assert(offsetof(DispatchKArgs, src) % 64 == 0, "per-rank records on 64-byte boundaries");
 
 // Kernel arguments of the combine kernel, passed by value.  The fields every
 // workgroup reads before its first row load come first and contiguous, so

@@ -175,7 +175,7 @@ __device__ __forceinline__ void write_slot(const DispatchKArgs& a, uint8_t* part
 // the run-time test alone cost ~2% on the DeepSeek-V3-shaped dispatch.
 template <bool DEVN>
 __device__ __forceinline__ int step_count(const DispatchKArgs& a, const int s, const bool first) {
-  if (!DEVN) return a.n[s];
+  if (!DEVN) return a.src[s].n;
   const int c = a.dev_n[s];
   const int ns = c < 0 ? 0 : (c > a.tpr ? a.tpr : c);
   if (first && threadIdx.x == 0) a.counts[s] = ns;
@@ -192,13 +192,13 @@ __device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const int r
   const int K = a.top_k;
   const int ns = step_count<DEVN>(a, s, t == 0 && blockIdx.y == 0);
   const bool real = t < ns;
-  const int32_t* __restrict__ idr = a.ids[s] + (int64_t)t * K;
+  const int32_t* __restrict__ idr = a.src[s].ids + (int64_t)t * K;
   const int64_t nv = a.hidden_bytes / VB;
   const int64_t per_block = (int64_t)a.block * U;
   // A padding row (t >= n_s) has no source row: its resource has size 0, so
   // the hardware discards its loads (they return 0 and touch no memory).
   const __amdgpu_buffer_rsrc_t src =
-      row_rsrc(a.hidden[s] + (int64_t)t * a.hidden_bytes, real ? a.hidden_bytes : 0);
+      row_rsrc(a.src[s].hidden + (int64_t)t * a.hidden_bytes, real ? a.hidden_bytes : 0);
   const int64_t c_first = (int64_t)blockIdx.y * per_block;
 
   // The first chunk of the token's hidden row is loaded before the routing
@@ -222,10 +222,10 @@ __device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const int r
   if (blockIdx.y == 0) {
     if (threadIdx.x == 0) {
       a.route[r] = m;
-      if (!DEVN && real) a.tokens[a.token_start[s] + t] = TokenRec{m, s, t};
+      if (!DEVN && real) a.tokens[a.src[s].token_start + t] = TokenRec{m, s, t};
     }
     // ids / weights slot of row r on every rank.
-    const float* __restrict__ wr = a.has_weights ? a.weights[s] + (int64_t)t * K : nullptr;
+    const float* __restrict__ wr = a.has_weights ? a.src[s].weights + (int64_t)t * K : nullptr;
     const int slots = a.ep * K;
     for (int i = threadIdx.x; i < slots; i += a.block) {
       const int d = i / K;
@@ -237,7 +237,7 @@ __device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const int r
       const int64_t dst_off = a.off_scale + (int64_t)r * S;
       if (a.scale_vec4) {
         const int64_t nw = S / 4;
-        const uint32_t* ssrc = reinterpret_cast<const uint32_t*>(a.scale[s] + (int64_t)t * S);
+        const uint32_t* ssrc = reinterpret_cast<const uint32_t*>(a.src[s].scale + (int64_t)t * S);
         for (int64_t c = threadIdx.x; c < nw; c += a.block) {
           const uint32_t x = ssrc[c];
           uint64_t mm = m;
@@ -248,7 +248,7 @@ __device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const int r
           }
         }
       } else {
-        const uint8_t* ssrc = a.scale[s] + (int64_t)t * S;
+        const uint8_t* ssrc = a.src[s].scale + (int64_t)t * S;
         for (int64_t c = threadIdx.x; c < S; c += a.block) {
           const uint8_t x = ssrc[c];
           uint64_t mm = m;
@@ -294,14 +294,14 @@ __device__ __forceinline__ void gather_stats_row(const DispatchKArgs& a, const i
   const int64_t B = a.eplb_bytes;
   const int64_t dst_off = a.off_eplb + (int64_t)s * B;
   if (a.eplb_vec4) {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.eplb[s]);
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(a.src[s].eplb);
     for (int64_t c = threadIdx.x; c < B / 4; c += blockDim.x) {
       const uint32_t x = src[c];
       for (int d = 0; d < a.ep; ++d)
         reinterpret_cast<uint32_t*>(a.ws + (int64_t)d * a.part_stride + dst_off)[c] = x;
     }
   } else {
-    const uint8_t* src = a.eplb[s];
+    const uint8_t* src = a.src[s].eplb;
     for (int64_t c = threadIdx.x; c < B; c += blockDim.x) {
       const uint8_t x = src[c];
       for (int d = 0; d < a.ep; ++d) (a.ws + (int64_t)d * a.part_stride + dst_off)[c] = x;
@@ -363,11 +363,11 @@ __device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const 
   const int K = a.top_k;
   const int ns = step_count<DEVN>(a, s, t == 0 && d == 0 && chunk == 0);
   const bool real = t < ns;
-  const int32_t* __restrict__ idr = a.ids[s] + (int64_t)t * K;
+  const int32_t* __restrict__ idr = a.src[s].ids + (int64_t)t * K;
 
   const int64_t nv = a.hidden_bytes / VB;
   const int64_t c0 = (int64_t)chunk * a.block * U;
-  const __amdgpu_buffer_rsrc_t src = row_rsrc(a.hidden[s] + (int64_t)t * a.hidden_bytes, a.hidden_bytes);
+  const __amdgpu_buffer_rsrc_t src = row_rsrc(a.src[s].hidden + (int64_t)t * a.hidden_bytes, a.hidden_bytes);
   int off[U];
   bool live[U];
   V v[U];
@@ -394,11 +394,11 @@ __device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const 
     // and weights stored from registers: 1.8% faster on the DeepSeek-V3
     // round than loading the row after the metadata stores.
     const __amdgpu_buffer_rsrc_t src_row =
-        row_rsrc(a.hidden[s] + (int64_t)t * a.hidden_bytes, real ? a.hidden_bytes : 0);
+        row_rsrc(a.src[s].hidden + (int64_t)t * a.hidden_bytes, real ? a.hidden_bytes : 0);
     const int lane = threadIdx.x & 63;
     if (real && lane < K) {
       e = (uint32_t)idr[lane];
-      if (a.has_weights) wv = a.weights[s][(int64_t)t * K + lane];
+      if (a.has_weights) wv = a.src[s].weights[(int64_t)t * K + lane];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -438,7 +438,7 @@ __device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const 
   if (chunk == 0) {
     if (d == 0 && threadIdx.x == 0) {
       a.route[r] = m;
-      if (!DEVN && real) a.tokens[a.token_start[s] + t] = TokenRec{m, s, t};
+      if (!DEVN && real) a.tokens[a.src[s].token_start + t] = TokenRec{m, s, t};
     }
     // This destination's ids / weights slot of row r.  LEAN: lane j of the
     // first wave stores slot j from its registers.  Otherwise written as
@@ -456,17 +456,17 @@ __device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const 
         const int64_t slot = (int64_t)r * K + jj;
         reinterpret_cast<int32_t*>(part + a.off_ids)[slot] = routed ? idr[jj] : a.invalid_id;
         if (a.has_weights)
-          reinterpret_cast<float*>(part + a.off_weights)[slot] = routed ? a.weights[s][(int64_t)t * K + jj] : 0.0f;
+          reinterpret_cast<float*>(part + a.off_weights)[slot] = routed ? a.src[s].weights[(int64_t)t * K + jj] : 0.0f;
       }
     }
     if (!LEAN && routed && a.scale_bytes) {
       const int64_t S = a.scale_bytes;
       uint8_t* dst = part + a.off_scale + (int64_t)r * S;
       if (a.scale_vec4) {
-        const uint32_t* ssrc = reinterpret_cast<const uint32_t*>(a.scale[s] + (int64_t)t * S);
+        const uint32_t* ssrc = reinterpret_cast<const uint32_t*>(a.src[s].scale + (int64_t)t * S);
         for (int64_t c = threadIdx.x; c < S / 4; c += a.block) reinterpret_cast<uint32_t*>(dst)[c] = ssrc[c];
       } else {
-        const uint8_t* ssrc = a.scale[s] + (int64_t)t * S;
+        const uint8_t* ssrc = a.src[s].scale + (int64_t)t * S;
         for (int64_t c = threadIdx.x; c < S; c += a.block) dst[c] = ssrc[c];
       }
     }

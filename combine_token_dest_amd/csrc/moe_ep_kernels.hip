@@ -21,11 +21,11 @@
 //   class description; routing: flashinfer.moe_ep.MoEEpCommunication,
 //   dispatch(); mask: NVLinkOneSidedAlltoAll, dispatch().
 //
-// combine: one workgroup per real token (s, t < n_s).  It reads the token's
-//   record and, for each 16-byte column chunk, loads the token's row from
-//   every destination rank (ascending), adds them in float32 in that order
-//   starting from +0.0, rounds once and stores the output row.  Rows of
-//   ranks the token did not reach are never read.
+// combine: one one-wave workgroup per (real token (s, t < n_s), 1 KiB column
+//   chunk).  It reads the token's record and loads its chunk of the token's
+//   row from every destination rank (ascending), adds them in float32 in
+//   that order starting from +0.0, rounds once and stores the output chunk.
+//   Rows of ranks the token did not reach are never read.
 //   flashinfer.moe_ep.MoEEpCommunication, combine().
 
 #include <hip/hip_runtime.h>
@@ -500,10 +500,11 @@ dispatch_dst_kernel(const DispatchKArgs a) {
 // ---------------------------------------------------------------------------
 // combine
 //
-// Grid: x = real token (prefix over sources), y = column chunk.  Each thread
-// owns U column vectors of VE elements; it loads them from up to DB
-// destination rows at a time (ascending rank) before adding, so one batch
-// covers every destination when the token reached at most DB ranks.
+// Grid (1-D): one workgroup per (token slot, column chunk), the chunks of a
+// token on one XCD (see combine_kernel).  Each thread owns U column vectors
+// of VE elements; it loads them from up to DB destination rows at a time
+// (ascending rank) before adding, so one batch covers every destination
+// when the token reached at most DB ranks.
 // ---------------------------------------------------------------------------
 // Raw storage of VE elements of a combine dtype.
 template <int DT, int VE> struct CVec;

@@ -24,7 +24,10 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep hipcc from fusing float adds into v_pk_add_f32.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# kernarg preload: the leading scalar kernel arguments arrive in scalar
+# registers at wave launch instead of through a load from the argument block.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-kernarg-preload-count=16"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall",
           f"-I{INCLUDE}", f"-I{CSRC}"]
 

@@ -105,9 +105,10 @@ struct DispatchKArgs {
 };
 static_assert(offsetof(DispatchKArgs, src) % 64 == 0, "per-rank records on 64-byte boundaries");
 
-// Kernel arguments of the combine kernel, passed by value.  The fields every
-// workgroup reads before its first row load come first and contiguous, so
-// they arrive in one batch of scalar loads; the per-rank tables follow.
+// Arguments of the combine kernel.  The launcher passes the fields every
+// workgroup needs before its first row load (chunk_div through eo_stride)
+// as leading scalar kernel arguments, preloaded into registers, and the
+// whole struct by value after them for the rest.
 struct CombineKArgs {
   OwnerDiv chunk_div;                       // workgroup index / 8 / chunks
   int32_t ntok;                             // token slots (slots past it store nothing)

@@ -50,11 +50,6 @@ template <> struct Bytes<2> { typedef uint16_t type; };
 template <> struct Bytes<1> { typedef uint8_t type; };
 
 
-// x / d for 0 <= x < 2^31, with the divisor's multiply-shift constants.
-__device__ __forceinline__ int divq(const OwnerDiv& od, int x) {
-  return (int)(((uint64_t)(uint32_t)x * od.magic) >> od.shift);
-}
-
 __device__ __forceinline__ int expert_owner(const OwnerDiv& od, uint32_t e) {
   return (int)(((uint64_t)e * od.magic) >> od.shift);
 }
@@ -169,28 +164,45 @@ __device__ __forceinline__ void write_slot(const DispatchKArgs& a, uint8_t* part
   }
 }
 
+// What a dispatch workgroup needs to find its item (row, destination,
+// chunk) and source rank.  These are the kernels' leading scalar arguments,
+// preloaded into scalar registers at wave launch, so the first memory access
+// of a workgroup is its source rank's argument record.  The four divisions
+// are multiply-shift constants (Granlund-Montgomery, as make_owner_div), the
+// four shift counts packed into one word so that all of it fits the
+// preloadable registers.
+struct DispatchHead {
+  uint64_t m_chunks, m_block_rows, m_ep, m_tpr;
+  uint32_t shifts;                     // bytes: chunks, block_rows, ep, tpr
+  int32_t dm_chunks, dm_block_rows, ep, tpr;
+};
+
+// x / d for 0 <= x < 2^31 with the multiply-shift constant of d and the
+// shift count in byte `which` of h.shifts.
+__device__ __forceinline__ int hdiv(uint64_t magic, uint32_t shifts, int which, int x) {
+  return (int)(((uint64_t)(uint32_t)x * magic) >> ((shifts >> (8 * which)) & 0xff));
+}
+
 // Token count of source rank s for this step.  DEVN: read from device memory
 // when the kernel runs (clamped to the rows the buffers hold) and recorded
 // for combine; else the host's count.  The two are separate instantiations:
 // the run-time test alone cost ~2% on the DeepSeek-V3-shaped dispatch.
 template <bool DEVN>
-__device__ __forceinline__ int step_count(const DispatchKArgs& a, const int s, const bool first) {
+__device__ __forceinline__ int step_count(const DispatchKArgs& a, const int s, const bool first, const int tpr) {
   if (!DEVN) return a.src[s].n;
   const int c = a.dev_n[s];
-  const int ns = c < 0 ? 0 : (c > a.tpr ? a.tpr : c);
+  const int ns = c < 0 ? 0 : (c > tpr ? tpr : c);
   if (first && threadIdx.x == 0) a.counts[s] = ns;
   return ns;
 }
 
 template <int VB, int U, int LP, int SP, bool DEVN>
-__device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const int r) {
+__device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const DispatchHead& h, const int r) {
   typedef typename Bytes<VB>::type V;
-  // (A division on the ALU: tpr arrives with the first batch of arguments,
-  // the multiply-shift constants would need a round trip of their own.)
-  const int s = r / a.tpr;
-  const int t = r - s * a.tpr;
+  const int s = hdiv(h.m_tpr, h.shifts, 3, r);
+  const int t = r - s * h.tpr;
   const int K = a.top_k;
-  const int ns = step_count<DEVN>(a, s, t == 0 && blockIdx.y == 0);
+  const int ns = step_count<DEVN>(a, s, t == 0 && blockIdx.y == 0, h.tpr);
   const bool real = t < ns;
   const int32_t* __restrict__ idr = a.src[s].ids + (int64_t)t * K;
   const int64_t nv = a.hidden_bytes / VB;
@@ -313,14 +325,17 @@ __device__ __forceinline__ void gather_stats_row(const DispatchKArgs& a, const i
 // rank when statistics are gathered; y = column chunk of the hidden row.
 template <int VB, int U, int LP, int SP, bool DEVN>
 __global__ void __launch_bounds__(kMaxBlock)
-dispatch_kernel(const DispatchKArgs a) {
+dispatch_kernel(const uint64_t m_chunks, const uint64_t m_block_rows, const uint64_t m_ep, const uint64_t m_tpr,
+                const uint32_t shifts, const int32_t dm_chunks, const int32_t dm_block_rows, const int32_t ep,
+                const int32_t tpr, const DispatchKArgs a) {
   // One workgroup per item (no grid-stride loop: a store of one item could
   // then alias the next item's loads, which keeps the compiler from using
   // scalar loads for the uniform ones).
-  const int rows = a.ep * a.tpr;
+  const DispatchHead h{m_chunks, m_block_rows, m_ep, m_tpr, shifts, dm_chunks, dm_block_rows, ep, tpr};
+  const int rows = ep * tpr;
   const int r = blockIdx.x;
   if (r < rows) {
-    dispatch_row<VB, U, LP, SP, DEVN>(a, r);
+    dispatch_row<VB, U, LP, SP, DEVN>(a, h, r);
   } else if (blockIdx.y == 0) {
     gather_stats_row(a, r - rows);
   }
@@ -342,26 +357,26 @@ dispatch_kernel(const DispatchKArgs a) {
 // ~0.3 us (1.6%) off the DeepSeek-V3-shaped dispatch in interleaved runs.
 // ---------------------------------------------------------------------------
 template <int VB, int U, int SP, bool DEVN, bool LEAN>
-__device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const int i) {
+__device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const DispatchHead& h, const int i) {
   typedef typename Bytes<VB>::type V;
   // 32-bit decode: the host keeps the item count below 2^31.
-  const int rows = a.ep * a.tpr;
+  const int rows = h.ep * h.tpr;
   const int x = i & 7;
   int k = i >> 3;
-  int k1 = divq(a.div_chunks, k);
-  const int chunk = k - k1 * a.dm_chunks;
+  int k1 = hdiv(h.m_chunks, h.shifts, 0, k);
+  const int chunk = k - k1 * h.dm_chunks;
   k = k1;
-  k1 = divq(a.div_block_rows, k);
-  const int j = k - k1 * a.dm_block_rows;
+  k1 = hdiv(h.m_block_rows, h.shifts, 1, k);
+  const int j = k - k1 * h.dm_block_rows;
   k = k1;
-  const int q = divq(a.div_ep, k);
-  const int d = k - q * a.ep;
-  const int r = x + 8 * (q * a.dm_block_rows + j);
+  const int q = hdiv(h.m_ep, h.shifts, 2, k);
+  const int d = k - q * h.ep;
+  const int r = x + 8 * (q * h.dm_block_rows + j);
   if (r >= rows) return;
-  const int s = divq(a.div_tpr, r);
-  const int t = r - s * a.tpr;
+  const int s = hdiv(h.m_tpr, h.shifts, 3, r);
+  const int t = r - s * h.tpr;
   const int K = a.top_k;
-  const int ns = step_count<DEVN>(a, s, t == 0 && d == 0 && chunk == 0);
+  const int ns = step_count<DEVN>(a, s, t == 0 && d == 0 && chunk == 0, h.tpr);
   const bool real = t < ns;
   const int32_t* __restrict__ idr = a.src[s].ids + (int64_t)t * K;
 
@@ -488,10 +503,13 @@ __device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const 
 // when statistics are gathered.
 template <int VB, int U, int SP, bool DEVN, bool LEAN>
 __global__ void __launch_bounds__(kMaxBlock)
-dispatch_dst_kernel(const DispatchKArgs a) {
+dispatch_dst_kernel(const uint64_t m_chunks, const uint64_t m_block_rows, const uint64_t m_ep, const uint64_t m_tpr,
+                    const uint32_t shifts, const int32_t dm_chunks, const int32_t dm_block_rows, const int32_t ep,
+                    const int32_t tpr, const DispatchKArgs a) {
+  const DispatchHead h{m_chunks, m_block_rows, m_ep, m_tpr, shifts, dm_chunks, dm_block_rows, ep, tpr};
   const int i = blockIdx.x;
   if (LEAN || i < a.dm_items) {
-    dispatch_dst_item<VB, U, SP, DEVN, LEAN>(a, i);
+    dispatch_dst_item<VB, U, SP, DEVN, LEAN>(a, h, i);
   } else {
     gather_stats_row(a, i - (int)a.dm_items);
   }
@@ -761,11 +779,9 @@ template <int VB, int U, bool DEVN> struct DestinationLeanKernel {
 hipError_t launch_dispatch(const DispatchKArgs& args, int vec_bytes, hipStream_t stream) {
   DispatchKArgs a = args;
   a.div_tpr = make_owner_div((uint32_t)std::max(1, a.tpr));
-  if (a.order == MOE_EP_ORDER_DESTINATION) {
-    a.div_chunks = make_owner_div((uint32_t)std::max(1, a.dm_chunks));
-    a.div_block_rows = make_owner_div((uint32_t)std::max(1, a.dm_block_rows));
-    a.div_ep = make_owner_div((uint32_t)std::max(1, a.ep));
-  }
+  a.div_chunks = make_owner_div((uint32_t)std::max(1, a.dm_chunks));
+  a.div_block_rows = make_owner_div((uint32_t)std::max(1, a.dm_block_rows));
+  a.div_ep = make_owner_div((uint32_t)std::max(1, a.ep));
   const int64_t extra = a.eplb_bytes ? a.ep : 0;
   const bool devn = a.dev_n != nullptr;
   const void* fn;
@@ -788,7 +804,11 @@ hipError_t launch_dispatch(const DispatchKArgs& args, int vec_bytes, hipStream_t
     a.block = sh.block;
   }
   if (!fn) return hipErrorInvalidValue;
-  void* kargs[] = {&a};
+  // The leading arguments (preloaded into scalar registers), then the rest.
+  uint64_t m_chunks = a.div_chunks.magic, m_block_rows = a.div_block_rows.magic;
+  uint64_t m_ep = a.div_ep.magic, m_tpr = a.div_tpr.magic;
+  uint32_t shifts = a.div_chunks.shift | a.div_block_rows.shift << 8 | a.div_ep.shift << 16 | a.div_tpr.shift << 24;
+  void* kargs[] = {&m_chunks, &m_block_rows, &m_ep, &m_tpr, &shifts, &a.dm_chunks, &a.dm_block_rows, &a.ep, &a.tpr, &a};
   return hipLaunchKernel(fn, grid, block, kargs, 0, stream);
 }
 

@@ -60,13 +60,16 @@ struct SourceRank {
 };
 static_assert(sizeof(SourceRank) == 64, "one cache line per source rank");
 
-// Kernel arguments of the dispatch kernels, passed by value.  The scalars
-// come first and contiguous, so a workgroup gets them in one batch of
-// scalar loads before it indexes the per-rank tables that follow (spread
-// over 3 KB of arguments, they had cost each workgroup a chain of dependent
-// scalar-cache round trips before its first data load).
+// Arguments of the dispatch kernels.  The launcher passes the item decode
+// (the div_* constants, the plan values, ep and tpr) as leading scalar
+// kernel arguments, preloaded into registers at wave launch, and this struct
+// by value after them.  Its scalars come first and contiguous, so a
+// workgroup gets the rest of them in one batch of scalar loads, together
+// with its source rank's record (spread over 3 KB of arguments, they had
+// cost each workgroup a chain of dependent scalar-cache round trips before
+// its first data load).
 struct DispatchKArgs {
-  OwnerDiv div_chunks;                 // destination-major decode: / dm_chunks
+  OwnerDiv div_chunks;                 // destination-major decode: / dm_chunks (set by the launcher)
   OwnerDiv div_block_rows;             //   / dm_block_rows
   OwnerDiv div_ep;                     //   / ep
   OwnerDiv div_tpr;                    // receive row r / tpr

@@ -542,6 +542,56 @@ def test_combine_input_layouts(layout):
     moe.destroy()
 
 
+@pytest.mark.parametrize("ep,cap,nt", [(3, 5, [5, 0, 3]), (5, 7, [7, 1, 0, 6, 2])])
+@pytest.mark.parametrize("order", ORDERS)
+def test_device_counts_with_a_partial_slot_group(ep, cap, nt, order):
+    """Device-resident counts with ep * tpr not a multiple of 8 (15 and 35
+    slots): combine's grid holds whole groups of 8 slots, and the slots past
+    the last one must store nothing.  Both combine input paths: the
+    library's buffers (constant stride) and per-rank tensors at uneven
+    offsets (the per-rank table)."""
+    name = f"devn_ep{ep}_cap{cap}"
+    full = random_case(zlib.crc32(name.encode()) % 10000, ep=ep, E=2 * ep, K=2, cap=cap, n=[cap] * ep,
+                       hidden_size=96, H=192, name=name)
+    for zero_copy in (True, False):
+        log(f"[parity] {name} device counts {nt}, order {order}, zero_copy {zero_copy}")
+        moe = parity.make_gpu(full, order=order)
+        hid, ids, wts, _ = parity.upload(full)
+        counts = torch.tensor(nt, dtype=torch.int32, device="cuda")
+        res = moe.dispatch(hid, ids, wts, local_num_tokens_device=counts)
+        c = dataclasses.replace(full, hidden=[h[:n] for h, n in zip(full.hidden, nt)],
+                                ids=[x[:n] for x, n in zip(full.ids, nt)],
+                                weights=[x[:n] for x, n in zip(full.weights, nt)])
+        om = oracle.OracleMoEEp(parity.oracle_params(c))
+        ores = om.dispatch(c.hidden, c.ids, c.weights, runtime_max_tokens_per_rank=cap)
+        eo_host = parity.combine_inputs_host(c, ores)
+        oout = om.combine(eo_host, "bf16")
+        torch.cuda.synchronize()
+        parity.compare_dispatch(c, res, ores, name)
+        if zero_copy:
+            eo = []
+            for d in range(ep):
+                buf = moe.get_combine_input_buffer(d, torch.bfloat16)
+                buf.copy_(parity.host_to_torch(eo_host[d], "bf16").view(buf.shape))
+                eo.append(buf)
+        else:
+            n_el = eo_host[0].size
+            big = torch.full((ep * (n_el + 64) + 64 * ep * ep,), float("nan"), dtype=torch.bfloat16, device="cuda")
+            eo, off = [], 0
+            for d in range(ep):
+                v = big[off:off + n_el].view(eo_host[d].shape)
+                v.copy_(parity.host_to_torch(eo_host[d], "bf16").view(eo_host[d].shape))
+                eo.append(v)
+                off += n_el + 64 + 64 * d
+        outs = [torch.full((cap, full.hidden_size), 7.0, dtype=torch.bfloat16, device="cuda") for _ in range(ep)]
+        moe.combine(eo, output=outs)
+        torch.cuda.synchronize()
+        parity.compare_combine(c, [outs[s][:nt[s]] for s in range(ep)], oout, name)
+        for s in range(ep):      # rows past the count are left alone
+            assert (outs[s][nt[s]:].float() == 7.0).all()
+        moe.destroy()
+
+
 # --------------------------------------------------------------------------
 # Call protocol on the GPU path
 # --------------------------------------------------------------------------

@@ -679,12 +679,16 @@ __device__ __forceinline__ void combine_token(const CombineKArgs& a, const Combi
 #pragma unroll
         for (int u = 0; u < U; ++u) unpack_add<DT, VE>(v[k][u], acc[u], k < cnt);
     };
-    // A token that reached at most DB/2 ranks loads only DB/2 rows (a
-    // uniform branch): 20% faster on a ragged round of 8 KiB rows (2.8 ranks
-    // per token), even on the others.
+    // A token that reached at most 2 (DB/2) ranks loads only 2 (DB/2) rows
+    // (a uniform branch): on a ragged round of 8 KiB rows (2.8 ranks per
+    // token) the 4-row batch made combine 20% faster and the 2-row one
+    // another 1.6%; the other workloads are even.  (A 6-row batch for 5 or 6
+    // ranks was slower on the 16- and 32-rank rounds.)
     // A batch needs at least one row: its first slot is the one every
     // unused slot repeats.  A token that reached no rank takes no batch.
-    if (mm != 0 && __builtin_popcountll(mm) <= DB / 2) {
+    if (mm != 0 && __builtin_popcountll(mm) <= 2) {
+      batch(std::integral_constant<int, 2>{});
+    } else if (mm != 0 && __builtin_popcountll(mm) <= DB / 2) {
       batch(std::integral_constant<int, DB / 2>{});
     } else {
       while (mm) batch(std::integral_constant<int, DB>{});

@@ -81,6 +81,22 @@ MUTANTS = [
      "None if gathered is None else (gathered.copy() if d == 0 else np.zeros_like(gathered))"),
     ("weights of routed rows zeroed", "moe_ep.py",
      "                            out_w[r] = w_s[t]", "                            out_w[r] = 0.0"),
+    ("65 ranks accepted", "moe_ep.py",
+     "if not (1 <= self.ep_size <= MAX_RANKS):", "if not (1 <= self.ep_size <= MAX_RANKS + 1):"),
+    ("0 ranks accepted", "moe_ep.py",
+     "if not (1 <= self.ep_size <= MAX_RANKS):", "if not (0 <= self.ep_size <= MAX_RANKS):"),
+    ("expert count not a multiple of ep_size accepted", "moe_ep.py",
+     "if self.num_experts < self.ep_size or self.num_experts % self.ep_size:",
+     "if self.num_experts < self.ep_size:"),
+    ("top_k 0 accepted", "moe_ep.py", "if self.top_k < 1 or", "if self.top_k < 0 or"),
+    ("negative capacity accepted", "moe_ep.py",
+     "self.max_tokens_per_rank < 0 or", "self.max_tokens_per_rank < -1 or"),
+    ("scales all-or-none not checked", "moe_ep.py",
+     "        if has_s and any(x is None for x in hidden_states_scale):\n", "        if False:\n"),
+    ("scales accepted without scale_row_bytes", "moe_ep.py",
+     "        if has_s and p.scale_row_bytes == 0:\n", "        if False:\n"),
+    ("unknown combine dtype accepted", "moe_ep.py",
+     "if dtype not in (\"f32\", \"bf16\", \"f16\"):", "if dtype not in (\"f32\", \"bf16\", \"f16\", \"f64\"):"),
     ("bf16 widened by an 8-bit shift", "numerics.py",
      "<< np.uint32(16)).view(np.float32)", "<< np.uint32(8)).view(np.float32)"),
     ("bf16 ties rounded away from zero", "numerics.py",

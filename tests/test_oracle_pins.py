@@ -420,6 +420,106 @@ def test_weights_absent_everywhere_is_allowed():
     assert res[0].topk_weights is None
 
 
+def _params(**kw):
+    base = dict(ep_size=2, num_experts=4, top_k=2, max_tokens_per_rank=4, hidden_size=2,
+                hidden_row_bytes=4)
+    base.update(kw)
+    return Params(**base)
+
+
+@pytest.mark.parametrize("kw", [
+    # The active-rank mask is one uint64, one bit per rank
+    # (NVLinkOneSidedAlltoAll, active_rank_mask()): 1..64 ranks.
+    dict(ep_size=0, num_experts=4), dict(ep_size=65, num_experts=65), dict(ep_size=-1),
+    # Contiguous ownership of equal blocks (the reading of "ranks that own
+    # its selected experts", MoEEpCommunication, dispatch()) needs a positive
+    # multiple of ep_size.
+    dict(num_experts=3), dict(num_experts=6, ep_size=4), dict(num_experts=1, ep_size=2),
+    dict(num_experts=0),
+    # A token selects at least one expert (topk_ids is [local_num_tokens,
+    # top_k], MoEEpCommunication, dispatch()); capacity, combine row size and
+    # dispatched row size are sizes.
+    dict(top_k=0), dict(top_k=-3), dict(max_tokens_per_rank=-1), dict(hidden_size=0),
+    dict(hidden_row_bytes=0), dict(scale_row_bytes=-4),
+], ids=lambda kw: ",".join(f"{k}={v}" for k, v in kw.items()))
+def test_params_rules_reject(kw):
+    with pytest.raises(OracleError) as e:
+        OracleMoEEp(_params(**kw))
+    assert e.value.kind == "invalid_arg"
+
+
+@pytest.mark.parametrize("kw", [
+    dict(ep_size=1, num_experts=1), dict(ep_size=64, num_experts=64), dict(ep_size=64, num_experts=128),
+    dict(num_experts=2), dict(top_k=1), dict(top_k=9), dict(max_tokens_per_rank=0),
+    dict(scale_row_bytes=0), dict(scale_row_bytes=8), dict(hidden_size=1, hidden_row_bytes=1),
+], ids=lambda kw: ",".join(f"{k}={v}" for k, v in kw.items()))
+def test_params_rules_accept(kw):
+    OracleMoEEp(_params(**kw))
+
+
+def test_ep_64_routes_to_rank_63():
+    """At the largest group the top mask bit is a real rank: expert E-1 lives
+    on rank 63 (NVLinkOneSidedAlltoAll, active_rank_mask(): a uint64 mask)."""
+    p = _params(ep_size=64, num_experts=128, max_tokens_per_rank=1)
+    o = OracleMoEEp(p)
+    hid = [np.full((1, 4), s, np.uint8) for s in range(64)]
+    ids = [np.array([[127, 0]], np.int32) for _ in range(64)]
+    res = o.dispatch(hid, ids, None)
+    for d in range(64):
+        want = d in (0, 63)
+        assert bool(res[d].valid.all()) == want
+        assert bool(res[d].valid.any()) == want
+
+
+def test_scales_all_or_none():
+    """hidden_states_scale travels row-aligned with hidden_states
+    (MoEEpCommunication, dispatch()), under the same every-rank-or-none rule
+    as the weights (NVLinkOneSidedAlltoAll, dispatch()).  Ranks with no
+    tokens still pass an empty [0, scale_row_bytes] array."""
+    p, hid, ids, w = _small()
+    p.scale_row_bytes = 3
+    scl = [np.arange(6, dtype=np.uint8).reshape(2, 3), np.arange(10, 13, dtype=np.uint8).reshape(1, 3)]
+    for partial in ([scl[0], None], [None, scl[1]]):
+        with pytest.raises(OracleError) as e:
+            OracleMoEEp(p).dispatch(hid, ids, w, hidden_states_scale=partial)
+        assert e.value.kind == "invalid_arg"
+    res = OracleMoEEp(p).dispatch(hid, ids, w, hidden_states_scale=scl)
+    # token (0, 0) has experts 0 and 2: ranks 0 and 1; token (1, 0) experts 2, 3: rank 1
+    np.testing.assert_array_equal(res[0].hidden_scale[0], scl[0][0])
+    np.testing.assert_array_equal(res[1].hidden_scale[4], scl[1][0])
+    res = OracleMoEEp(p).dispatch(hid, ids, w, hidden_states_scale=[None, None])
+    assert res[0].hidden_scale is None
+
+
+def test_scales_need_scale_row_bytes():
+    """Scale rows are sized at creation (the pages' params); a step that
+    passes scales to a group created without them is refused."""
+    p, hid, ids, w = _small()
+    assert p.scale_row_bytes == 0
+    scl = [np.zeros((2, 0), np.uint8), np.zeros((1, 0), np.uint8)]
+    with pytest.raises(OracleError) as e:
+        OracleMoEEp(p).dispatch(hid, ids, w, hidden_states_scale=scl)
+    assert e.value.kind == "invalid_arg"
+    scl = [np.zeros((2, 4), np.uint8), np.zeros((1, 4), np.uint8)]
+    with pytest.raises(OracleError) as e:
+        OracleMoEEp(p).dispatch(hid, ids, w, hidden_states_scale=scl)
+    assert e.value.kind == "invalid_arg"
+
+
+@pytest.mark.parametrize("dtype", ["f64", "bytes", "fp8", "F32", "", "bfloat16"])
+def test_combine_rejects_unknown_dtype(dtype):
+    """The combine element types are float32, bfloat16 and float16; any
+    other name is refused before anything is summed, and the dispatch stays
+    pending (MoEEpCommunication, combine(): one combine per dispatch)."""
+    p, hid, ids, w = _small()
+    o = OracleMoEEp(p)
+    o.dispatch(hid, ids, w)
+    with pytest.raises(OracleError) as e:
+        o.combine([np.zeros((8, 2), np.float32)] * 2, dtype)
+    assert e.value.kind == "invalid_arg"
+    o.combine([np.zeros((8, 2), np.float32)] * 2, "f32")
+
+
 # --------------------------------------------------------------------------
 # bfloat16 rounding against torch's CPU conversion
 # --------------------------------------------------------------------------

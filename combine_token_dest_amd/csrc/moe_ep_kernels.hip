@@ -655,7 +655,11 @@ __device__ __forceinline__ void combine_token(const CombineKArgs& a, const Combi
     // and add +0.0.
     auto batch = [&](auto dbx) {
       constexpr int DBX = decltype(dbx)::value;
+      // Every slot starts as a size-0 resource (its loads return 0 and touch
+      // no memory), so no path can load through an unset one.
       __amdgpu_buffer_rsrc_t rows[DBX];
+#pragma unroll
+      for (int k = 0; k < DBX; ++k) rows[k] = row_rsrc(h.eo_base, 0);
       int cnt = 0;
 #pragma unroll
       for (int k = 0; k < DBX; ++k) {
@@ -665,8 +669,8 @@ __device__ __forceinline__ void combine_token(const CombineKArgs& a, const Combi
           const uint8_t* eo = STRIDED ? h.eo_base + (int64_t)d * h.eo_stride : a.expert_output[d];
           rows[k] = row_rsrc(eo + r * row_bytes, row_bytes);
           cnt = k + 1;
-        } else {
-          rows[k] = rows[k > 0 ? k - 1 : 0];
+        } else if (k > 0) {
+          rows[k] = rows[k - 1];
         }
       }
       V v[DBX][U];

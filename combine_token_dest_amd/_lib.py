@@ -39,8 +39,10 @@ EXPORTS = [
     "moe_ep_is_platform_supported", "moe_ep_workspace_bytes", "moe_ep_create", "moe_ep_dispatch",
     "moe_ep_get_combine_input_buffer", "moe_ep_combine", "moe_ep_destroy",
     "moe_ep_create_vmm", "moe_ep_workspace", "moe_ep_checkpoint_prepare", "moe_ep_checkpoint_restore",
-    "moe_ep_active_rank_mask", "moe_ep_status_string", "moe_ep_last_error",
+    "moe_ep_dispatch_noalloc", "moe_ep_active_rank_mask", "moe_ep_status_string", "moe_ep_last_error",
 ]
+
+MOE_EP_NOALLOC_MAX_ROWS = 65536
 
 R = MOE_EP_MAX_RANKS
 
@@ -126,6 +128,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_ep_checkpoint_prepare.restype = c_int
     lib.moe_ep_checkpoint_restore.argtypes = [c_void_p]
     lib.moe_ep_checkpoint_restore.restype = c_int
+    lib.moe_ep_dispatch_noalloc.argtypes = [c_void_p, POINTER(moe_ep_dispatch_args),
+                                            POINTER(moe_ep_dispatch_result), c_void_p]
+    lib.moe_ep_dispatch_noalloc.restype = c_int
     lib.moe_ep_active_rank_mask.argtypes = [POINTER(c_int32), c_int32, POINTER(c_uint64)]
     lib.moe_ep_active_rank_mask.restype = c_int
     lib.moe_ep_status_string.argtypes = [c_int]
@@ -172,6 +177,14 @@ def moe_ep_dispatch(handle: int, args: moe_ep_dispatch_args, ep_size: int,
     results = (moe_ep_dispatch_result * ep_size)()
     _check(load().moe_ep_dispatch(c_void_p(handle), byref(args), results, c_void_p(stream)),
            "moe_ep_dispatch")
+    return list(results)
+
+
+def moe_ep_dispatch_noalloc(handle: int, args: moe_ep_dispatch_args, ep_size: int,
+                            stream: int) -> List[moe_ep_dispatch_result]:
+    results = (moe_ep_dispatch_result * ep_size)()
+    _check(load().moe_ep_dispatch_noalloc(c_void_p(handle), byref(args), results, c_void_p(stream)),
+           "moe_ep_dispatch_noalloc")
     return list(results)
 
 

@@ -159,6 +159,9 @@ struct moe_ep_handle_s {
   OwnerDiv owner;
   int state;
   // Remembered from the dispatch for its combine.
+  uint64_t* route;     // where the dispatch left its destination masks,
+  TokenRec* tokens;    //   token records
+  int32_t* counts;     //   and device-step counts (workspace or fixed area)
   int32_t tpr;
   int32_t n[MOE_EP_MAX_RANKS];
   uint64_t mask;       // as passed (MOE_EP_ALL_RANKS = none)
@@ -317,6 +320,12 @@ int moe_ep_create(const moe_ep_params* params, void* workspace, size_t workspace
   h->ws = static_cast<uint8_t*>(workspace);
   h->owner = make_owner_div((uint32_t)(params->num_experts / params->ep_size));
   h->device = workspace_device(workspace);
+  if (h->device >= 0) {
+    // Set-up of the fixed record area for moe_ep_dispatch_noalloc on this
+    // device; a failure here is reported by that call, which looks again.
+    NoallocArea area;
+    if (noalloc_scratch(h->device, &area) != hipSuccess) (void)hipGetLastError();
+  }
   h->checked_stream = nullptr;
   h->state = kIdle;
   h->tpr = 0;
@@ -427,8 +436,10 @@ static int check_mask(const moe_ep_params& p, uint64_t mask) {
   return MOE_EP_OK;
 }
 
-int moe_ep_dispatch(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispatch_result* results,
-                    void* stream) {
+namespace {
+
+int dispatch_impl(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispatch_result* results,
+                  void* stream, bool noalloc) {
   if (!h || !a || !results) return fail(MOE_EP_ERR_INVALID_ARG, "NULL handle, args or results");
   const moe_ep_params& p = h->p;
   const int ep = p.ep_size;
@@ -517,8 +528,30 @@ int moe_ep_dispatch(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispa
     }
   }
   k.dev_n = a->local_num_tokens_device;
-  k.counts = reinterpret_cast<int32_t*>(h->ws + h->L.off_counts);
-  k.tokens = reinterpret_cast<TokenRec*>(h->ws + h->L.off_tokens);
+  if (noalloc) {
+    // The records go to the library's fixed array on the workspace's device.
+    if ((int64_t)ep * tpr > MOE_EP_NOALLOC_MAX_ROWS)
+      return fail(MOE_EP_ERR_CAPACITY, "ep_size * tokens_per_rank = %lld exceeds the %d rows of the fixed record area",
+                  (long long)ep * tpr, MOE_EP_NOALLOC_MAX_ROWS);
+    int dev = h->device;
+    if (dev < 0) {
+      const hipError_t e = hipGetDevice(&dev);
+      if (e != hipSuccess) return fail(MOE_EP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    }
+    NoallocArea area;
+    const hipError_t e = noalloc_scratch(dev, &area);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(MOE_EP_ERR_HIP, "fixed record area on device %d: %s", dev, hipGetErrorString(e));
+    }
+    k.counts = area.counts;
+    k.tokens = area.tokens;
+    k.route = area.route;
+  } else {
+    k.counts = reinterpret_cast<int32_t*>(h->ws + h->L.off_counts);
+    k.tokens = reinterpret_cast<TokenRec*>(h->ws + h->L.off_tokens);
+    k.route = reinterpret_cast<uint64_t*>(h->ws + h->L.off_route);
+  }
   for (int s = 0, start = 0; s < ep; ++s) {
     k.src[s].token_start = start;
     start += host_n[s];
@@ -528,7 +561,6 @@ int moe_ep_dispatch(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispa
   k.eplb_vec4 = has_e && (eplb_align_or % 4 == 0);
 
   k.ws = h->ws;
-  k.route = reinterpret_cast<uint64_t*>(h->ws + h->L.off_route);
   k.part_stride = h->L.part_stride;
   k.off_hidden = h->L.off_hidden;
   k.off_scale = h->L.off_scale;
@@ -554,6 +586,9 @@ int moe_ep_dispatch(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispa
   if (e != hipSuccess) return fail(MOE_EP_ERR_HIP, "dispatch launch failed: %s", hipGetErrorString(e));
 
   h->state = kDispatched;
+  h->route = k.route;
+  h->tokens = k.tokens;
+  h->counts = k.counts;
   h->tpr = tpr;
   for (int s = 0; s < MOE_EP_MAX_RANKS; ++s) h->n[s] = s < ep ? host_n[s] : 0;
   h->mask = a->active_rank_mask;
@@ -570,6 +605,18 @@ int moe_ep_dispatch(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispa
     results[d].dispatch_order = k.order;
   }
   return ok();
+}
+
+}  // namespace
+
+int moe_ep_dispatch(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispatch_result* results,
+                    void* stream) {
+  return dispatch_impl(h, a, results, stream, false);
+}
+
+int moe_ep_dispatch_noalloc(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispatch_result* results,
+                            void* stream) {
+  return dispatch_impl(h, a, results, stream, true);
 }
 
 int moe_ep_get_combine_input_buffer(moe_ep_handle h, int32_t rank, int32_t dtype, void** out_ptr) {
@@ -637,10 +684,10 @@ int moe_ep_combine(moe_ep_handle h, const moe_ep_combine_args* a, void* stream) 
   k.token_start[ep] = total;
   // After a device-count dispatch, h->n holds tpr for every rank (the most
   // any rank can have); the kernel reads the counts that dispatch used.
-  k.dev_counts = h->device_counts ? reinterpret_cast<const int32_t*>(h->ws + h->L.off_counts) : nullptr;
+  k.dev_counts = h->device_counts ? h->counts : nullptr;
   const int vec_elems = (int)(pow2_divisor(align_or, 16) / esz);
-  k.route = reinterpret_cast<const uint64_t*>(h->ws + h->L.off_route);
-  k.tokens = reinterpret_cast<const TokenRec*>(h->ws + h->L.off_tokens);
+  k.route = h->route;
+  k.tokens = h->tokens;
   k.hidden = p.hidden_size;
   k.tpr = h->tpr;
   k.ep = ep;

@@ -191,6 +191,19 @@ hipError_t launch_combine(const CombineKArgs& a, int dtype, int vec_elems, hipSt
 // Multiply-shift constants for x / d with 0 <= x < 2^31 (host code).
 OwnerDiv make_owner_div(uint32_t d);
 
+// Where moe_ep_dispatch_noalloc keeps the records its combine reads: the
+// library's fixed device array on one GPU (MOE_EP_NOALLOC_MAX_ROWS rows).
+struct NoallocArea {
+  uint64_t* route;     // [MOE_EP_NOALLOC_MAX_ROWS] destination masks
+  TokenRec* tokens;    // [MOE_EP_NOALLOC_MAX_ROWS] token records
+  int32_t* counts;     // [MOE_EP_MAX_RANKS] counts of a device-count step
+  int64_t bytes;       // size of the array
+};
+
+// The array's address on `device` (looked up once per device, with that
+// device current; later calls return the kept address).  Host code.
+hipError_t noalloc_scratch(int device, NoallocArea* out);
+
 // Whether the non-NULL entries of p[0..n) lie at *base + d * *stride (host code).
 bool common_stride(const uint8_t* const* p, int n, const uint8_t** base, int64_t* stride);
 

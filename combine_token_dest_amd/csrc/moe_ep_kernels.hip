@@ -32,6 +32,8 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "moe_ep_internal.h"
@@ -863,6 +865,62 @@ hipError_t launch_combine(const CombineKArgs& args, int dtype, int vec_elems, hi
   int64_t hidden = a.hidden;
   void* kargs[] = {&magic, &shift, &a.ntok, &a.chunks, &a.block, &tokens, &eo_base, &eo_stride, &hidden, &a};
   return hipLaunchKernel(fn, dim3(sh.grid_x), dim3(sh.block), kargs, 0, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Fixed record area of moe_ep_dispatch_noalloc
+//
+// The destination masks, token records and counts a dispatch leaves for its
+// combine, kept in the library instead of the workspace: route masks
+// [kNoallocRows] u64, then token records [kNoallocRows] TokenRec, then
+// counts [kMaxRanks] int32.  Each GPU the library runs on holds its own copy
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// never the device memory: kernels get the address noalloc_scratch() looked
+// up for the device.
+// ---------------------------------------------------------------------------
+constexpr int64_t kNoallocRows = MOE_EP_NOALLOC_MAX_ROWS;
+constexpr int64_t kNoallocTokensOff = kNoallocRows * 8;
+constexpr int64_t kNoallocCountsOff = kNoallocTokensOff + kNoallocRows * (int64_t)sizeof(TokenRec);
+constexpr int64_t kNoallocBytes = kNoallocCountsOff + kMaxRanks * 4;
+static_assert(kNoallocTokensOff % 16 == 0 && kNoallocCountsOff % 16 == 0, "aligned sub-arrays");
+
+static __device__ __align__(256) uint8_t scratch[kNoallocBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<uint8_t*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+}  // namespace
+
+hipError_t noalloc_scratch(int device, NoallocArea* out) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  uint8_t* p = g_scratch_ptr[device].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[device].load(std::memory_order_relaxed);
+    if (!p) {
+      // The symbol's address on `device`, looked up with that device current.
+      int prev = -1;
+      hipError_t e = hipGetDevice(&prev);
+      if (e != hipSuccess) return e;
+      if (prev != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+      void* addr = nullptr;
+      e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (prev != device) {
+        const hipError_t e2 = hipSetDevice(prev);
+        if (e == hipSuccess) e = e2;
+      }
+      if (e != hipSuccess) return e;
+      if (!addr) return hipErrorInvalidSymbol;
+      p = static_cast<uint8_t*>(addr);
+      g_scratch_ptr[device].store(p, std::memory_order_release);
+    }
+  }
+  out->route = reinterpret_cast<uint64_t*>(p);
+  out->tokens = reinterpret_cast<TokenRec*>(p + kNoallocTokensOff);
+  out->counts = reinterpret_cast<int32_t*>(p + kNoallocCountsOff);
+  out->bytes = kNoallocBytes;
+  return hipSuccess;
 }
 
 }  // namespace moe_ep_detail

@@ -140,7 +140,8 @@ class MoEEp:
                  hidden_states_scale: Optional[Sequence[Optional[torch.Tensor]]] = None,
                  runtime_max_tokens_per_rank: Optional[int] = None,
                  eplb_local_stats=None, active_rank_mask=None,
-                 local_num_tokens_device: Optional[torch.Tensor] = None) -> List[DispatchResult]:
+                 local_num_tokens_device: Optional[torch.Tensor] = None,
+                 noalloc: bool = False) -> List[DispatchResult]:
         """Send every token to the ranks owning its experts; see
         include/moe_ep.h, moe_ep_dispatch.
 
@@ -148,7 +149,11 @@ class MoEEp:
         makes the kernels read the token counts when they run, so a captured
         graph can replay steps with other counts.  Every per-rank buffer must
         then hold ``tokens_per_rank`` rows (the runtime bound, else the
-        capacity), and so do the combine outputs."""
+        capacity), and so do the combine outputs.
+
+        ``noalloc=True`` calls moe_ep_dispatch_noalloc: the same dispatch,
+        with the records combine reads kept in the library's fixed device
+        array (steps of at most MOE_EP_NOALLOC_MAX_ROWS receive rows)."""
         if self._handle is None:
             raise RuntimeError("MoEEp has been destroyed")
         p = self.params
@@ -217,7 +222,8 @@ class MoEEp:
             else int(runtime_max_tokens_per_rank)
         a.active_rank_mask = _mask_value(active_rank_mask)
         stream = torch.cuda.current_stream(self.device).cuda_stream
-        res = _lib.moe_ep_dispatch(self._handle, a, ep, stream)
+        entry = _lib.moe_ep_dispatch_noalloc if noalloc else _lib.moe_ep_dispatch
+        res = entry(self._handle, a, ep, stream)
         self._tpr = res[0].tokens_per_rank if ep else 0
         self._buffer_dtype = None
         # the copy order the library chose for this step ("source" / "destination")

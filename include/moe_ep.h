@@ -266,6 +266,31 @@ MOE_EP_API int moe_ep_checkpoint_prepare(moe_ep_handle handle);
  * handle is unusable, as above. */
 MOE_EP_API int moe_ep_checkpoint_restore(moe_ep_handle handle);
 
+/* Receive rows (ep_size * tokens_per_rank) of the largest step
+ * moe_ep_dispatch_noalloc takes: the size of the library's fixed record area
+ * (24 bytes per row plus 256, 1.5 MiB, held on each GPU the library runs on
+ * until the process ends). */
+#define MOE_EP_NOALLOC_MAX_ROWS 65536
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * dispatch as moe_ep_dispatch -- same arguments, results, state change and
+ * errors -- except that the per-token routing records dispatch leaves for
+ * combine (destination masks, token positions, token counts) go to a fixed
+ * device array inside the library instead of the workspace.  The handle's
+ * next moe_ep_combine reads them from there.  Nothing is allocated or freed:
+ * the array's device address is looked up once per device (at moe_ep_create
+ * when the workspace's device is known, else at the first call on a device).
+ * ERR_CAPACITY when ep_size * tokens_per_rank exceeds MOE_EP_NOALLOC_MAX_ROWS
+ * (nothing enqueued); ERR_HIP when the lookup fails.
+ * Every handle on a GPU shares that GPU's one array, and it keeps only the
+ * last noalloc dispatch's records: a noalloc dispatch must not run between
+ * another handle's noalloc dispatch and that handle's combine on the same
+ * GPU (in stream order), and calls that overlap on one GPU, from several
+ * streams or threads, race. */
+MOE_EP_API int moe_ep_dispatch_noalloc(moe_ep_handle handle, const moe_ep_dispatch_args* args,
+                                       moe_ep_dispatch_result* results, void* stream);
+
 /* Bitmask with bit r set for each of the n listed ranks, all in [0, 64)
  * (NVLinkOneSidedAlltoAll, active_rank_mask()).  ERR_MASK for a rank out of
  * range. */

@@ -22,6 +22,10 @@ hipError_t launch_combine(const CombineKArgs&, int, int, hipStream_t) {
   std::printf("launch_combine reached\n");
   return hipErrorInvalidValue;
 }
+hipError_t noalloc_scratch(int, NoallocArea*) {
+  std::printf("noalloc_scratch reached\n");
+  return hipErrorInvalidValue;
+}
 }  // namespace moe_ep_detail
 
 namespace {
@@ -235,6 +239,10 @@ int main() {
   a.runtime_max_tokens_per_rank = 1 << 19;
   a.active_rank_mask = MOE_EP_ALL_RANKS;
   expect(moe_ep_dispatch(h, &a, res, nullptr) == MOE_EP_ERR_INVALID_ARG, "grid limit");
+  // The same step is past the fixed record area of the noalloc dispatch.
+  expect(moe_ep_dispatch_noalloc(h, &a, res, nullptr) == MOE_EP_ERR_CAPACITY, "noalloc area");
+  a.runtime_max_tokens_per_rank = MOE_EP_NOALLOC_MAX_ROWS / 64 + 1;
+  expect(moe_ep_dispatch_noalloc(h, &a, res, nullptr) == MOE_EP_ERR_CAPACITY, "noalloc area + 1 token");
   expect(moe_ep_destroy(h) == MOE_EP_OK, "destroy 2");
 
   int32_t ranks[] = {0, 5, 63};

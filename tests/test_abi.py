@@ -95,7 +95,7 @@ def test_constants_match_header():
     """Every MOE_EP_* constant of the binding has the header's value, and
     the header defines no constant the binding lacks."""
     text = open(HEADER).read()
-    names = sorted(set(re.findall(r"\b(MOE_EP_(?:OK|ERR_\w+|F32|BF16|F16|ORDER_\w+|MAX_RANKS|ALL_RANKS))\b",
+    names = sorted(set(re.findall(r"\b(MOE_EP_(?:OK|ERR_\w+|F32|BF16|F16|ORDER_\w+|MAX_RANKS|ALL_RANKS|NOALLOC_MAX_ROWS))\b",
                                   text)))
     lines = ["#include <stdio.h>", '#include "moe_ep.h"', "int main(void) {"]
     lines += [f'printf("{n} %llu\\n", (unsigned long long)(long long)({n}));' for n in names
@@ -187,10 +187,12 @@ def dispatch_args(n, *, ids=True, hidden=True, weights=None, rtpr=-1, mask=_lib.
     return a
 
 
-def test_dispatch_validation(lib):
+@pytest.mark.parametrize("entry", ["moe_ep_dispatch", "moe_ep_dispatch_noalloc"])
+def test_dispatch_validation(lib, entry):
+    """Both dispatch entry points validate alike, before any device work."""
     p = params()
     h = _lib.moe_ep_create(p, FAKE_WS, _lib.moe_ep_workspace_bytes(p))
-    D = _lib.moe_ep_dispatch
+    D = getattr(_lib, entry)
     cases = [
         (dispatch_args([17, 0, 0, 0]), _lib.MOE_EP_ERR_CAPACITY),            # n > capacity
         (dispatch_args([5, 0, 3, 0], rtpr=4), _lib.MOE_EP_ERR_CAPACITY),     # rtpr < largest n
@@ -215,6 +217,27 @@ def test_dispatch_validation(lib):
     assert status_of(_lib.moe_ep_combine, h, ca, 0) == _lib.MOE_EP_ERR_STATE
     assert status_of(_lib.moe_ep_get_combine_input_buffer, h, 0, _lib.MOE_EP_F32) == _lib.MOE_EP_ERR_STATE
     _lib.moe_ep_destroy(h)
+
+
+def test_noalloc_dispatch_rejects_steps_past_the_fixed_area(lib):
+    """moe_ep_dispatch_noalloc keeps its records in a fixed area of
+    MOE_EP_NOALLOC_MAX_ROWS receive rows: a larger step is refused on the
+    host with ERR_CAPACITY (no device work, the handle stays idle)."""
+    p = params(ep_size=64, num_experts=64, top_k=1, max_tokens_per_rank=1025, hidden_size=4,
+               hidden_row_bytes=16)
+    h = _lib.moe_ep_create(p, FAKE_WS, _lib.moe_ep_workspace_bytes(p))
+    a = _lib.moe_ep_dispatch_args()
+    a.runtime_max_tokens_per_rank = -1              # capacity: 64 x 1025 rows
+    a.active_rank_mask = _lib.MOE_EP_ALL_RANKS
+    assert status_of(_lib.moe_ep_dispatch_noalloc, h, a, 64, 0) == _lib.MOE_EP_ERR_CAPACITY
+    assert "fixed record area" in _lib.moe_ep_last_error()
+    a.runtime_max_tokens_per_rank = 1025
+    assert status_of(_lib.moe_ep_dispatch_noalloc, h, a, 64, 0) == _lib.MOE_EP_ERR_CAPACITY
+    ca = _lib.moe_ep_combine_args()
+    ca.active_rank_mask = _lib.MOE_EP_ALL_RANKS
+    assert status_of(_lib.moe_ep_combine, h, ca, 0) == _lib.MOE_EP_ERR_STATE
+    _lib.moe_ep_destroy(h)
+    assert 64 * 1024 == _lib.MOE_EP_NOALLOC_MAX_ROWS
 
 
 def test_eplb_validation(lib):

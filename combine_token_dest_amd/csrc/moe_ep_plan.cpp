@@ -137,6 +137,7 @@ bool common_stride(const uint8_t* const* p, int n, const uint8_t** base, int64_t
 // waited on a longer chain of argument loads, also needed two resident
 // generations of workgroups to win.
 constexpr int64_t kDmBlockBytes = 512 * 1024;
+constexpr int64_t kDmXcdRows = 4;            // the kernels' kXcdRows
 constexpr int64_t kDmAutoMaxPairs = 16384;   // ep * ep * tpr
 constexpr int kDmAutoMaxRanks = 16;
 
@@ -147,9 +148,12 @@ bool plan_dispatch(DispatchKArgs& a, int vec_bytes, int requested) {
   a.dm_items = 0;
   if (requested == MOE_EP_ORDER_SOURCE_ROW) return true;
   if (automatic && (a.ep > kDmAutoMaxRanks || rows * a.ep > kDmAutoMaxPairs)) return true;
-  const int64_t rmax = (rows + 7) / 8;
+  // Rows per XCD (the kernel hands rows to the XCDs in blocks of
+  // kDmXcdRows), and rows per XCD block, a multiple of kDmXcdRows.
+  const int64_t rmax = (rows + 8 * kDmXcdRows - 1) / (8 * kDmXcdRows) * kDmXcdRows;
   int64_t b = kDmBlockBytes / std::max<int64_t>(1, a.hidden_bytes);
-  b = std::max<int64_t>(1, std::min<int64_t>(b, std::max<int64_t>(1, rmax)));
+  b = std::min<int64_t>(b, std::max<int64_t>(kDmXcdRows, rmax)) / kDmXcdRows * kDmXcdRows;
+  b = std::max<int64_t>(kDmXcdRows, b);
   const int64_t nq = rmax > 0 ? (rmax + b - 1) / b : 0;
   const LaunchShape tile = row_tile(0, a.hidden_bytes / vec_bytes);
   const int64_t nv = a.hidden_bytes / vec_bytes;

@@ -15,10 +15,11 @@ bench rotates over --instances independent copies (workspace, inputs,
 outputs); each DeepSeek-V3-shaped instance touches ~265 MB, 8 of them ~2 GB.
 
 Printed: one JSON line with the whole-job throughput (algorithmic bytes per
-round / wall time per round, the driver's metric), the dominant kernel's
-roofline figures from HIP events recorded around every launch on the launch
-stream, and the CPU oracle's throughput on a bounded sample of the same
-workload.
+round / wall time per round over the K timed steps), each kernel's share of
+the HBM peak and the slower (dominant) kernel's roofline figures from HIP
+events on the launch stream (a separate pass of K steps whose launches queue
+behind a spin kernel, so the events time the kernels alone), and the CPU
+oracle's throughput on a bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -54,21 +55,27 @@ def log(msg):
 # ---------------------------------------------------------------------------
 # algorithmic bytes
 # ---------------------------------------------------------------------------
+BYTES_FORMULA = ("dispatch N*(4K(1+w)+H+S) + P*(H+S+4K*w) + R*4K; combine N*4K + P*O + N*O "
+                 "(N tokens, P routed (token, rank) pairs, R = ep*ep*tpr receive rows, w = weights present)")
+
+
 def algorithmic_bytes(w, n, masks, tpr, has_w):
-    """Bytes the method must move in one round:
+    """Bytes the method must move in one round (BYTES_FORMULA):
     dispatch reads every real token's ids, weights, hidden and scale row once,
-    writes every routed (token, rank) pair's hidden and scale row, and writes
-    the ids (and weights) slot of every receive row of every rank; combine
-    reads every routed pair's expert row and writes every real token's output
-    row."""
+    writes every routed (token, rank) pair's hidden row, scale row and
+    weights, and the ids slot of every receive row of every rank (the
+    invalid id where the token did not go); combine reads what says where
+    each token went (its K ids' worth), every routed pair's expert row, and
+    writes every real token's output row.  The zero weights of invalid rows
+    and the route masks are not counted."""
     K, H, S = w.top_k, w.hidden_row_bytes, w.scale_row_bytes
     O = w.hidden_size * w.combine_elem_bytes
     N = sum(n)
     P = int(sum(bin(m).count("1") for m in masks))
     R = w.ep_size * w.ep_size * tpr
     wb = 1 if has_w else 0
-    b_dispatch = N * (4 * K * (1 + wb) + H + S) + P * (H + S) + R * 4 * K * (1 + wb)
-    b_combine = P * O + N * O
+    b_dispatch = N * (4 * K * (1 + wb) + H + S) + P * (H + S + 4 * K * wb) + R * 4 * K
+    b_combine = N * 4 * K + P * O + N * O
     return b_dispatch, b_combine, N, P, R
 
 
@@ -103,11 +110,18 @@ class Instance:
                          combine_max_elem_bytes=w.combine_elem_bytes,
                          enable_rank_mask=inp.active_rank_mask is not None, dispatch_order=order,
                          device=device)
-        hid, ids, wts, scl = [[t.clone() for t in lst] if lst is not None else None for lst in dev_inputs[:4]]
+        # The group's per-rank inputs and outputs each live in one allocation
+        # per instance ([ep, capacity, ...], rank s's rows at the start of
+        # slice s), as one process holding every rank would lay them out.
+        # (Per-rank tensors from torch's caching allocator landed wherever
+        # freed blocks were: the same dispatch then took 15.8-17.3 us from one
+        # instance to the next; in one allocation it takes 15.6-15.9.)
+        hid, ids, wts, scl = [grouped_copy(lst, w.ep_size, w.max_tokens_per_rank, device)
+                              if lst is not None else None for lst in dev_inputs[:4]]
         self.inputs = (hid, ids, wts, scl)
         self.cdtype = torch.float32 if w.combine_dtype == "f32" else torch.bfloat16
-        self.outputs = [torch.empty((n, w.hidden_size), dtype=self.cdtype, device=device)
-                        for n in inp.local_num_tokens]
+        out_all = torch.empty((w.ep_size, w.max_tokens_per_rank, w.hidden_size), dtype=self.cdtype, device=device)
+        self.outputs = [out_all[s, :n] for s, n in enumerate(inp.local_num_tokens)]
         rtpr = inp.runtime_max_tokens_per_rank
         mask = inp.active_rank_mask
         # First round through the Python API, with the expert stand-in in between.
@@ -156,6 +170,20 @@ class Instance:
         st = self.lib.moe_ep_combine(self.handle, ctypes.byref(self.cargs), stream)
         if st:
             raise RuntimeError(f"moe_ep_combine: {st} {self.lib.moe_ep_last_error().decode()}")
+
+
+def grouped_copy(per_rank, ep, cap, device):
+    """Copies of per-rank [n_s, ...] tensors as slices [s, :n_s] of one
+    [ep, cap, ...] allocation."""
+    import torch
+    t0 = per_rank[0]
+    alls = torch.empty((ep, cap) + tuple(t0.shape[1:]), dtype=t0.dtype, device=device)
+    views = []
+    for s, t in enumerate(per_rank):
+        v = alls[s, :t.shape[0]]
+        v.copy_(t)
+        views.append(v)
+    return views
 
 
 def expert_standin_torch(w, d, res, values, tpr, out):
@@ -250,6 +278,22 @@ class HipEvents:
 
     def destroy(self, ev):
         self.hip.hipEventDestroy(ev)
+
+
+def spin_cycles_for_us(us, stream):
+    """Argument of torch.cuda._sleep (a spin kernel that touches no memory)
+    for about `us` microseconds, from one timed spin on this device."""
+    import torch
+    probe = 1 << 20
+    torch.cuda._sleep(probe)                        # first launch: load the kernel
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    torch.cuda._sleep(probe)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per_us = probe / max(e0.elapsed_time(e1) * 1e3, 1e-3)
+    return int(per_us * us)
 
 
 def kernel_source_hash():
@@ -369,20 +413,29 @@ def main():
         insts[i % I].combine(sp)
     torch.cuda.synchronize()
 
-    # Timed region: K steps in groups of I (one per instance): the group's I
-    # dispatches back to back, then its I combines, so every instance still
-    # runs dispatch -> combine.  HIP events on the launch stream bracket each
-    # run of back-to-back launches; the kernels' launch latency, which a pair
-    # of events around a single launch would add, is then spread over I
-    # launches.
+    # Per-kernel passes (untimed for `value`).  Each queues its launches
+    # behind a spin kernel (no memory traffic) that runs long enough for the
+    # host to enqueue all of them, so no kernel waits for its launch call.
+    #  1. K steps in groups of I (one per instance): the group's I dispatches
+    #     back to back, then its I combines (every instance still runs
+    #     dispatch -> combine), with a HIP event before each run of
+    #     dispatches and of combines and after the last: t_d(g) and t_c(g).
+    #  2. K steps alternating as a caller would, one event at each end: R,
+    #     the time per round (dispatch + combine).
+    # An event costs the stream some idle time of its own (m per event,
+    # unknown), so t_d(g) = n_g * D + m and t_c(g) = n_g * C + m; with
+    # D + C = R this gives m and the per-launch kernel times D and C.
     K = args.steps
     sizes = [I] * (K // I) + ([K % I] if K % I else [])
     G = len(sizes)
     hev = HipEvents()
     ev = [[hev.create() for _ in range(3)] for _ in range(G)]
-    log(f"[bench] timing {K} steps ({G} groups of up to {I})")
+    ea, eb = hev.create(), hev.create()
+    spin_cycles = spin_cycles_for_us(max(1000.0, 12.0 * (2 * K + 3 * G)), stream)
+    log(f"[bench] per-kernel passes: {K} steps ({G} groups of up to {I}), then {K} alternating")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    torch.cuda._sleep(spin_cycles)
     for g in range(G):
         e = ev[g]
         group = insts[:sizes[g]]
@@ -396,17 +449,29 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall_s = t1 - t0
-    d_ms = np.array([hev.elapsed_ms(ev[g][0], ev[g][1]) / sizes[g] for g in range(G)])
-    c_ms = np.array([hev.elapsed_ms(ev[g][1], ev[g][2]) / sizes[g] for g in range(G)])
-    # per-kernel means weighted by launches
+    torch.cuda._sleep(spin_cycles)
+    hev.record(ea, sp)
+    for i in range(K):
+        insts[i % I].dispatch(sp)
+        insts[i % I].combine(sp)
+    hev.record(eb, sp)
+    torch.cuda.synchronize()
+    round_ms = hev.elapsed_ms(ea, eb) / K
+    td = np.array([hev.elapsed_ms(ev[g][0], ev[g][1]) for g in range(G)])
+    tc = np.array([hev.elapsed_ms(ev[g][1], ev[g][2]) for g in range(G)])
     w_g = np.array(sizes, dtype=float)
-    for e in ev:
+    marker_ms = max(0.0, float(td.sum() + tc.sum() - K * round_ms) / (2 * G))
+    d_ms = (td - marker_ms) / w_g            # per-launch times of each group
+    c_ms = (tc - marker_ms) / w_g
+    for e in ev + [[ea, eb]]:
         for x in e:
             hev.destroy(x)
 
-    # The same K steps without events, alternating dispatch and combine per
-    # instance as a caller would: this pass gives the step time and `value`
-    # (the grouped pass above attributes time to each kernel).
+    # Timed region: K steps without events, alternating dispatch and combine
+    # per instance as a caller would, bracketed by synchronizations: this pass
+    # gives the step time and `value` (the pass above attributes time to each
+    # kernel).
+    log(f"[bench] timing {K} steps")
     torch.cuda.synchronize()
     t2 = time.perf_counter()
     for i in range(K):
@@ -486,10 +551,12 @@ def main():
     d_gbs, c_gbs = b_d / (d_us * 1e-6) / 1e9, b_c / (c_us * 1e-6) / 1e9
     # kernel names as rocprofv3 lists them (template arguments aside)
     dname = "dispatch_dst_kernel" if insts[0].order == "destination" else "dispatch_kernel"
+    # The dominant kernel is the slower one (the larger share of the round).
     dominant = dname if d_us >= c_us else "combine_kernel"
     dom_bytes, dom_us, dom_gbs = (b_d, d_us, d_gbs) if dominant == dname else (b_c, c_us, c_gbs)
     # The counters were taken on the workloads as defined, not at other capacities.
-    traffic = read_traffic(w.name, dname, dominant) if args.tokens_per_rank is None else None
+    traffic = {k: read_traffic(w.name, dname, k) if args.tokens_per_rank is None else None
+               for k in (dname, "combine_kernel")}
 
     copy_info = None
     if not args.no_copy_calibration:
@@ -537,7 +604,11 @@ def main():
         "us_per_round_kernels": round(d_us + c_us, 2),
         "us_per_round_kernels_p10_p50_p90": [round(float(np.percentile(d_ms + c_ms, q)) * 1e3, 2)
                                              for q in (10, 50, 90)],
-        "timing": "kernel times from fence-free HIP events around runs of I back-to-back launches",
+        "timing": "kernel times from fence-free HIP events around runs of I back-to-back launches and "
+                  "around K alternating rounds, queued behind a spin kernel; each event's own stream time "
+                  "(marker_us) solved out",
+        "marker_us": round(marker_ms * 1e3, 3),
+        "us_per_round_events": round(round_ms * 1e3, 3),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "pct_hbm_peak_kernels": round(100 * bytes_round / ((d_us + c_us) * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
         "bytes_per_round": bytes_round,
@@ -546,11 +617,13 @@ def main():
             dname: {"us_mean": round(d_us, 3), "us_p10": round(float(np.percentile(d_ms, 10)) * 1e3, 3),
                                 "us_p50": round(float(np.median(d_ms)) * 1e3, 3),
                                 "us_p90": round(float(np.percentile(d_ms, 90)) * 1e3, 3),
-                                "bytes": b_d, "GB/s": round(d_gbs, 1)},
+                                "bytes": b_d, "GB/s": round(d_gbs, 1),
+                                "frac": round(d_gbs / HBM_PEAK_GBS, 4), "traffic": traffic[dname]},
             "combine_kernel": {"us_mean": round(c_us, 3), "us_p10": round(float(np.percentile(c_ms, 10)) * 1e3, 3),
                                "us_p50": round(float(np.median(c_ms)) * 1e3, 3),
                                "us_p90": round(float(np.percentile(c_ms, 90)) * 1e3, 3),
-                               "bytes": b_c, "GB/s": round(c_gbs, 1)},
+                               "bytes": b_c, "GB/s": round(c_gbs, 1),
+                               "frac": round(c_gbs / HBM_PEAK_GBS, 4), "traffic": traffic["combine_kernel"]},
         },
         "us_per_round_grouped_with_events": round(wall_s / K * 1e6, 2),
         "us_per_round_graph_replay": graph_us,
@@ -558,8 +631,9 @@ def main():
         "us_per_round_two_streams": two_stream_us,
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": dom_bytes,
-                     "us_per_launch": round(dom_us, 3)},
+                     "traffic": traffic[dominant], "algorithmic_bytes_per_launch": dom_bytes,
+                     "us_per_launch": round(dom_us, 3), "bytes_formula": BYTES_FORMULA,
+                     "timing": "HIP events around runs of back-to-back launches queued behind a spin kernel, event overhead solved out"},
         "cpu_baseline": cpu,
         "kernel_code_sha256": kernel_source_hash(),
     }

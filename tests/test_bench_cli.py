@@ -29,9 +29,13 @@ def test_algorithmic_bytes_hand_counted():
     b_d, b_c, N, P, R = bench.algorithmic_bytes(w, [2, 1], [0b01, 0b11, 0b00], 2, True)
     assert (N, P, R) == (3, 3, 8)
     reads = 3 * (4 * 2 * 2 + 100 + 8)       # ids + weights + hidden + scale of each real token
-    writes = 3 * (100 + 8) + 8 * 4 * 2 * 2  # routed rows + the ids/weights slot of every receive row
+    writes = 3 * (100 + 8 + 4 * 2) + 8 * 4 * 2  # routed rows with their weights + the ids slot of every receive row
     assert b_d == reads + writes
-    assert b_c == 3 * 20 + 3 * 20           # routed expert rows in, output rows out
+    assert b_c == 3 * 4 * 2 + 3 * 20 + 3 * 20   # where each token went (K ids), routed expert rows in, outputs out
+    # without weights: no weight bytes read or written
+    b_d0, b_c0, *_ = bench.algorithmic_bytes(w, [2, 1], [0b01, 0b11, 0b00], 2, False)
+    assert b_d0 == 3 * (4 * 2 + 100 + 8) + 3 * (100 + 8) + 8 * 4 * 2
+    assert b_c0 == b_c
 
 
 def test_routed_pairs_match_the_oracle():

@@ -190,3 +190,51 @@ def test_noalloc_at_the_largest_step():
     finally:
         a.destroy()
         b.destroy()
+
+
+@pytest.mark.parametrize("name", ["dsv3", "ragged"])
+def test_noalloc_round_replays_from_a_graph(name):
+    """The callers the entry point is for capture it: a noalloc dispatch and
+    its combine captured in one HIP graph, replayed on new inputs written in
+    place (eager work and synchronisations between the replays), every
+    replay equal to the oracle's round."""
+    w = wl.BY_NAME[name]
+    print(f"[noalloc] graph {name}", flush=True)
+    c0 = _case(name)
+    moe = parity.make_gpu(c0)
+    try:
+        hid, ids, wts, sc = parity.upload(c0)
+        tdt = torch.float32 if c0.combine_dtype == "f32" else torch.bfloat16
+        tpr = c0.rtpr if c0.rtpr is not None else w.max_tokens_per_rank
+        rows = w.ep_size * tpr
+        eo = [torch.zeros((rows, w.hidden_size), dtype=tdt, device="cuda") for _ in range(w.ep_size)]
+        outs = [torch.empty((n, w.hidden_size), dtype=tdt, device="cuda") for n in c0.n]
+        kw = dict(hidden_states_scale=sc, runtime_max_tokens_per_rank=c0.rtpr, active_rank_mask=c0.mask)
+        moe.dispatch(hid, ids, wts, noalloc=True, **kw)
+        moe.combine(eo, output=outs, active_rank_mask=c0.mask)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            res = moe.dispatch(hid, ids, wts, noalloc=True, **kw)
+            moe.combine(eo, output=outs, active_rank_mask=c0.mask)
+        torch.cuda.synchronize()
+        for i, seed in enumerate([21, 22, 23]):
+            # same token counts as the captured step (host counts are baked in)
+            c = parity.case_from_workload(w, local_num_tokens=c0.n, seed=seed)
+            ores, eo_host, oout = _oracle(c)
+            for s in range(w.ep_size):
+                if c.n[s]:
+                    hid[s].copy_(torch.from_numpy(c.hidden[s]))
+                    ids[s].copy_(torch.from_numpy(c.ids[s]))
+                    wts[s].copy_(torch.from_numpy(c.weights[s]))
+                    if sc is not None:
+                        sc[s].copy_(torch.from_numpy(c.scale[s]))
+            for d in range(w.ep_size):
+                eo[d].copy_(parity.host_to_torch(eo_host[d], c.combine_dtype))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            parity.compare_dispatch(c, res, ores, f"{name} noalloc replay {i}")
+            parity.compare_combine(c, outs, oout, f"{name} noalloc replay {i}")
+    finally:
+        moe.destroy()

@@ -280,6 +280,18 @@ class HipEvents:
         self.hip.hipEventDestroy(ev)
 
 
+def solve_kernel_times(td, tc, n, round_ms):
+    """Per-launch dispatch and combine times of each group from the grouped
+    pass: td[g] = n[g] * D + m and tc[g] = n[g] * C + m, where m is the
+    stream time one event costs, and D + C = round_ms (the alternating pass).
+    Summing over the G groups, sum(td) + sum(tc) = K * round_ms + 2 * G * m
+    with K = sum(n).  Returns (per-group D, per-group C, m), m clamped at 0."""
+    td, tc, n = (np.asarray(x, dtype=float) for x in (td, tc, n))
+    G, K = len(n), float(n.sum())
+    m = max(0.0, float(td.sum() + tc.sum() - K * round_ms) / (2 * G))
+    return (td - m) / n, (tc - m) / n, m
+
+
 def spin_cycles_for_us(us, stream):
     """Argument of torch.cuda._sleep (a spin kernel that touches no memory)
     for about `us` microseconds, from one timed spin on this device."""
@@ -460,9 +472,7 @@ def main():
     td = np.array([hev.elapsed_ms(ev[g][0], ev[g][1]) for g in range(G)])
     tc = np.array([hev.elapsed_ms(ev[g][1], ev[g][2]) for g in range(G)])
     w_g = np.array(sizes, dtype=float)
-    marker_ms = max(0.0, float(td.sum() + tc.sum() - K * round_ms) / (2 * G))
-    d_ms = (td - marker_ms) / w_g            # per-launch times of each group
-    c_ms = (tc - marker_ms) / w_g
+    d_ms, c_ms, marker_ms = solve_kernel_times(td, tc, w_g, round_ms)
     for e in ev + [[ea, eb]]:
         for x in e:
             hev.destroy(x)

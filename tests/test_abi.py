@@ -315,3 +315,98 @@ def test_destination_order_grid_limit(lib):
     ca.active_rank_mask = _lib.MOE_EP_ALL_RANKS
     assert status_of(_lib.moe_ep_combine, h, ca, 0) == _lib.MOE_EP_ERR_STATE
     _lib.moe_ep_destroy(h)
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="valid steps would launch kernels on the fake workspace")
+def test_validation_agrees_with_the_oracle(lib):
+    """The library's host validation and the oracle's rules, written
+    separately from the same passages, accept and refuse the same steps:
+    random small groups with counts past the capacity, runtime bounds on
+    either side, masks with and without enable_rank_mask and with bits past
+    ep_size, and weights / scales passed by all, none or some ranks.  A step
+    both accept gets as far as the kernel launch, which fails on a host with
+    no GPU (MOE_EP_ERR_HIP) before anything runs; one with no receive rows
+    launches nothing and succeeds."""
+    import numpy as np
+    from hypothesis import given, settings, strategies as st, HealthCheck
+    import oracle
+
+    kinds = {"capacity": _lib.MOE_EP_ERR_CAPACITY, "mask": _lib.MOE_EP_ERR_MASK,
+             "invalid_arg": _lib.MOE_EP_ERR_INVALID_ARG}
+
+    @st.composite
+    def steps(draw):
+        ep = draw(st.integers(1, 6))
+        epr = draw(st.integers(1, 3))
+        K = draw(st.integers(1, 4))
+        cap = draw(st.integers(0, 5))
+        n = [draw(st.integers(0, cap + 1)) for _ in range(ep)]
+        rtpr = draw(st.one_of(st.none(), st.integers(0, cap + 1)))
+        enable = draw(st.booleans())
+        mask = draw(st.one_of(st.none(), st.integers(0, (1 << (ep + 1)) - 1)))
+        S = draw(st.sampled_from([0, 8]))
+        wsel = draw(st.sampled_from(["all", "none", "some"]))
+        ssel = draw(st.sampled_from(["all", "none", "some"]))
+        return ep, epr, K, cap, n, rtpr, enable, mask, S, wsel, ssel
+
+    def present(sel, ep, s):
+        return sel == "all" or (sel == "some" and s != ep - 1)
+
+    @settings(max_examples=400, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+    @given(steps())
+    def check(step):
+        ep, epr, K, cap, n, rtpr, enable, mask, S, wsel, ssel = step
+        if wsel == "some" and ep == 1:
+            wsel = "none"
+        if ssel == "some" and ep == 1:
+            ssel = "none"
+        H = 8
+        # the oracle
+        P = oracle.Params(ep, ep * epr, K, cap, 2, H, S, -1, enable)
+        hid = [np.zeros((k, H), np.uint8) for k in n]
+        ids = [np.zeros((k, K), np.int32) for k in n]
+        wts = [np.zeros((k, K), np.float32) if present(wsel, ep, s) else None for s, k in enumerate(n)]
+        scl = [np.zeros((k, S), np.uint8) if present(ssel, ep, s) else None for s, k in enumerate(n)]
+        try:
+            oracle.OracleMoEEp(P).dispatch(hid, ids, wts if wsel != "none" else None,
+                                           hidden_states_scale=scl if ssel != "none" else None,
+                                           runtime_max_tokens_per_rank=rtpr, active_rank_mask=mask)
+            # a step of no receive rows launches nothing and succeeds
+            want = _lib.MOE_EP_OK if (cap if rtpr is None else rtpr) == 0 else _lib.MOE_EP_ERR_HIP
+        except oracle.OracleError as e:
+            want = kinds[e.kind]
+        # the library
+        p = params(ep_size=ep, num_experts=ep * epr, top_k=K, max_tokens_per_rank=cap, hidden_size=2,
+                   hidden_row_bytes=H, scale_row_bytes=S, enable_rank_mask=1 if enable else 0)
+        h = _lib.moe_ep_create(p, FAKE_WS, _lib.moe_ep_workspace_bytes(p))
+        try:
+            a = _lib.moe_ep_dispatch_args()
+            for s, k in enumerate(n):
+                a.local_num_tokens[s] = k
+                if k:
+                    a.hidden[s] = FAKE_WS + 4096 * (s + 1)
+                    a.topk_ids[s] = FAKE_WS + 4096 * (s + 100)
+                if present(wsel, ep, s) and wsel != "none":
+                    a.weights_present |= 1 << s
+                    if k:
+                        a.topk_weights[s] = FAKE_WS + 4096 * (s + 200)
+                if present(ssel, ep, s) and ssel != "none":
+                    a.scales_present |= 1 << s
+                    if k:
+                        a.hidden_scale[s] = FAKE_WS + 4096 * (s + 300)
+            a.runtime_max_tokens_per_rank = -1 if rtpr is None else rtpr
+            a.active_rank_mask = _lib.MOE_EP_ALL_RANKS if mask is None else mask
+            got = status_of(_lib.moe_ep_dispatch, h, a, ep, 0)
+        finally:
+            _lib.moe_ep_destroy(h)
+        assert got == want, (step, _lib.moe_ep_last_error())
+
+    check()

@@ -38,6 +38,23 @@ def test_algorithmic_bytes_hand_counted():
     assert b_c0 == b_c
 
 
+def test_event_overhead_is_solved_out():
+    """Groups of n launches timed with one event each: t = n * D + m.  The
+    alternating pass gives D + C; the solve recovers D, C and m exactly,
+    also for a short last group."""
+    D, C, m = 15.9, 17.0, 3.3
+    n = np.array([8, 8, 4])
+    td, tc = n * D + m, n * C + m
+    d, c, mm = bench.solve_kernel_times(td, tc, n, D + C)
+    np.testing.assert_allclose(d, D)
+    np.testing.assert_allclose(c, C)
+    assert abs(mm - m) < 1e-12
+    # no event overhead at all: nothing subtracted
+    d, c, mm = bench.solve_kernel_times(n * D, n * C, n, D + C)
+    assert mm == 0.0
+    np.testing.assert_allclose(d, D)
+
+
 def test_routed_pairs_match_the_oracle():
     w = wl.BY_NAME["dsv3"]
     inp = wl.make_inputs(w)

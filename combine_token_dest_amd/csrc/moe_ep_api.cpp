@@ -533,10 +533,16 @@ int dispatch_impl(moe_ep_handle h, const moe_ep_dispatch_args* a, moe_ep_dispatc
     if ((int64_t)ep * tpr > MOE_EP_NOALLOC_MAX_ROWS)
       return fail(MOE_EP_ERR_CAPACITY, "ep_size * tokens_per_rank = %lld exceeds the %d rows of the fixed record area",
                   (long long)ep * tpr, MOE_EP_NOALLOC_MAX_ROWS);
+    // The device the kernels will run on: the workspace's, else the
+    // stream's (the current device's for the null stream).
     int dev = h->device;
     if (dev < 0) {
-      const hipError_t e = hipGetDevice(&dev);
-      if (e != hipSuccess) return fail(MOE_EP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+      const hipError_t e =
+          stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) : hipGetDevice(&dev);
+      if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MOE_EP_ERR_HIP, "device of the stream: %s", hipGetErrorString(e));
+      }
     }
     NoallocArea area;
     const hipError_t e = noalloc_scratch(dev, &area);

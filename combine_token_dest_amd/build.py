@@ -63,5 +63,23 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+C_ROUND_SRC = os.path.join(ROOT, "tests", "host", "c_round.c")
+C_ROUND_BIN = os.path.join(ROOT, "tests", "host", "c_round")
+
+
+def build_c_round() -> str:
+    """Compile tests/host/c_round.c, a round through the C ABI alone (plain
+    C99 with the HIP runtime's C API), linked against LIB_PATH."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(HIPCC)))
+    tmp = C_ROUND_BIN + ".tmp"
+    _run(["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+          f"-I{rocm}/include", f"-I{INCLUDE}", C_ROUND_SRC, f"-L{PKG_DIR}", "-lmoe_ep",
+          f"-L{rocm}/lib", "-lamdhip64", "-lm",
+          "-Wl,-rpath,$ORIGIN/../../combine_token_dest_amd", f"-Wl,-rpath,{rocm}/lib", "-o", tmp])
+    os.replace(tmp, C_ROUND_BIN)
+    return C_ROUND_BIN
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_c_round())

@@ -351,6 +351,8 @@ def main():
     ap.add_argument("--tokens-per-rank", type=int, default=None,
                     help="the workload at another capacity (tokens per rank), e.g. decode batch sizes")
     ap.add_argument("--instances", type=int, default=8)
+    ap.add_argument("--kernel-steps", type=int, default=160,
+                    help="steps of each per-kernel timing pass (at least --steps)")
     ap.add_argument("--dispatch-order", default="auto", choices=["auto", "source", "destination"],
                     help="copy order of the dispatch kernel (the library picks by shape under auto)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -419,32 +421,38 @@ def main():
     sp = stream.cuda_stream
     I = len(insts)
 
-    log(f"[bench] warmup {args.warmup}")
-    for i in range(args.warmup):
-        insts[i % I].dispatch(sp)
-        insts[i % I].combine(sp)
+    # First launches of every instance (module load, first-touch of the
+    # workspaces), untimed; the W warm-up steps run right before the timed
+    # region below.
+    log("[bench] one round on each instance")
+    for inst in insts:
+        inst.dispatch(sp)
+        inst.combine(sp)
     torch.cuda.synchronize()
 
-    # Per-kernel passes (untimed for `value`).  Each queues its launches
-    # behind a spin kernel (no memory traffic) that runs long enough for the
-    # host to enqueue all of them, so no kernel waits for its launch call.
-    #  1. K steps in groups of I (one per instance): the group's I dispatches
-    #     back to back, then its I combines (every instance still runs
-    #     dispatch -> combine), with a HIP event before each run of
+    # Per-kernel passes (untimed for `value`), of KP = max(K, --kernel-steps)
+    # steps each so that the split between the kernels does not rest on a
+    # few groups.  Each queues its launches behind a spin kernel (no memory
+    # traffic) that runs long enough for the host to enqueue all of them, so
+    # no kernel waits for its launch call.
+    #  1. KP steps in groups of I (one per instance): the group's I
+    #     dispatches back to back, then its I combines (every instance still
+    #     runs dispatch -> combine), with a HIP event before each run of
     #     dispatches and of combines and after the last: t_d(g) and t_c(g).
-    #  2. K steps alternating as a caller would, one event at each end: R,
+    #  2. KP steps alternating as a caller would, one event at each end: R,
     #     the time per round (dispatch + combine).
     # An event costs the stream some idle time of its own (m per event,
     # unknown), so t_d(g) = n_g * D + m and t_c(g) = n_g * C + m; with
     # D + C = R this gives m and the per-launch kernel times D and C.
     K = args.steps
-    sizes = [I] * (K // I) + ([K % I] if K % I else [])
+    KP = max(K, args.kernel_steps)
+    sizes = [I] * (KP // I) + ([KP % I] if KP % I else [])
     G = len(sizes)
     hev = HipEvents()
     ev = [[hev.create() for _ in range(3)] for _ in range(G)]
     ea, eb = hev.create(), hev.create()
-    spin_cycles = spin_cycles_for_us(max(1000.0, 12.0 * (2 * K + 3 * G)), stream)
-    log(f"[bench] per-kernel passes: {K} steps ({G} groups of up to {I}), then {K} alternating")
+    spin_cycles = spin_cycles_for_us(max(1000.0, 12.0 * (2 * KP + 3 * G)), stream)
+    log(f"[bench] per-kernel passes: {KP} steps ({G} groups of up to {I}), then {KP} alternating")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     torch.cuda._sleep(spin_cycles)
@@ -463,12 +471,12 @@ def main():
     wall_s = t1 - t0
     torch.cuda._sleep(spin_cycles)
     hev.record(ea, sp)
-    for i in range(K):
+    for i in range(KP):
         insts[i % I].dispatch(sp)
         insts[i % I].combine(sp)
     hev.record(eb, sp)
     torch.cuda.synchronize()
-    round_ms = hev.elapsed_ms(ea, eb) / K
+    round_ms = hev.elapsed_ms(ea, eb) / KP
     td = np.array([hev.elapsed_ms(ev[g][0], ev[g][1]) for g in range(G)])
     tc = np.array([hev.elapsed_ms(ev[g][1], ev[g][2]) for g in range(G)])
     w_g = np.array(sizes, dtype=float)
@@ -477,11 +485,17 @@ def main():
         for x in e:
             hev.destroy(x)
 
-    # Timed region: K steps without events, alternating dispatch and combine
-    # per instance as a caller would, bracketed by synchronizations: this pass
-    # gives the step time and `value` (the pass above attributes time to each
-    # kernel).
-    log(f"[bench] timing {K} steps")
+    # W untimed warm-up steps, then the timed region: K steps without
+    # events, alternating dispatch and combine per instance as a caller
+    # would, bracketed by synchronizations: this pass gives the step time and
+    # `value` (the passes above attribute time to each kernel).  The warm-up
+    # sits right before the timed steps: after 1-100 ms of idle GPU (host
+    # work such as the solve above) a 20-step region measured ~0.5 us per
+    # step slower than one started on a part that had just been busy.
+    log(f"[bench] warmup {args.warmup}, then timing {K} steps")
+    for i in range(args.warmup):
+        insts[i % I].dispatch(sp)
+        insts[i % I].combine(sp)
     torch.cuda.synchronize()
     t2 = time.perf_counter()
     for i in range(K):
@@ -635,7 +649,8 @@ def main():
                                "bytes": b_c, "GB/s": round(c_gbs, 1),
                                "frac": round(c_gbs / HBM_PEAK_GBS, 4), "traffic": traffic["combine_kernel"]},
         },
-        "us_per_round_grouped_with_events": round(wall_s / K * 1e6, 2),
+        "us_per_round_grouped_with_events": round(wall_s / KP * 1e6, 2),
+        "kernel_steps": KP,
         "us_per_round_graph_replay": graph_us,
         "us_per_round_graph_replay_all_instances": graph_all_us,
         "us_per_round_two_streams": two_stream_us,

@@ -167,12 +167,18 @@ constexpr int kDispatchBlock = 128;      // dispatch threads per workgroup, at m
 constexpr int kCombineU = 1;             // combine: vectors per thread
 constexpr int kCombineDB = 8;            // combine: destination rows loaded per batch
 constexpr int kCombineBlock = 64;        // combine threads per workgroup, at most
+// Combine residency cap for long rows: LDS reserved per one-wave
+// workgroup so that at most 18 share a CU (160 KiB of LDS each), taken when
+// a token's row spans at least kCombineCapChunks column chunks.
+constexpr int kCombineCapLds = 9088;
+constexpr int64_t kCombineCapChunks = 12;
 
 struct LaunchShape {
   int grid_x;   // dispatch: rows; combine: workgroups (token slots rounded up to 8, x chunks)
   int grid_y;   // column chunks of a row (combine: per token, in the 1-D grid)
   int block;    // threads per workgroup
   int u;        // vectors per thread
+  int lds = 0;  // dynamic LDS bytes per workgroup, reserved only to cap residency (unused by the code)
 };
 
 // Fills a.order and the destination-major fields for a step: `requested` is

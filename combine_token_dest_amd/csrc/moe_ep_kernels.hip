@@ -883,7 +883,7 @@ hipError_t launch_combine(const CombineKArgs& args, int dtype, int vec_elems, hi
   int64_t eo_stride = a.eo_stride;
   int64_t hidden = a.hidden;
   void* kargs[] = {&magic, &shift, &a.ntok, &a.chunks, &a.block, &tokens, &eo_base, &eo_stride, &hidden, &a};
-  return hipLaunchKernel(fn, dim3(sh.grid_x), dim3(sh.block), kargs, 0, stream);
+  return hipLaunchKernel(fn, dim3(sh.grid_x), dim3(sh.block), kargs, (size_t)sh.lds, stream);
 }
 
 // ---------------------------------------------------------------------------

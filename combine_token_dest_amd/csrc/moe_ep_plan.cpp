@@ -78,6 +78,13 @@ LaunchShape dispatch_shape(int64_t rows, int64_t hidden_bytes, int vec_bytes) {
 // (A 2-D grid of (slots, chunks) keeps the XCD placement but sweeps chunk 0
 // of every token first: 4% slower on the DeepSeek-V3 round, 11% on a
 // 16-rank fp8 one.)
+// Rows of at least kCombineCapChunks chunks run with at most 18 workgroups
+// per CU (LDS reserved at launch, see kCombineCapLds) instead of 32: on
+// 14 KiB rows (8 ranks x 128 tokens, and 16 ranks x 256 tokens of fp8
+// dispatch) combine was 1.2-1.6% faster with 16-20 per CU, over three
+// boxes; on a ragged 8-rank round of 8 KiB rows (2.8 ranks per token, so
+// fewer row loads in flight per wave) 16-20 per CU were 3-5% slower and
+// 22-24 even.
 LaunchShape combine_shape(int64_t tokens, int64_t hidden, int vec_elems) {
   const int64_t nv = hidden / vec_elems;
   const int block = round_block(std::min<int64_t>(kCombineBlock, nv), kMaxCombineBlock);
@@ -85,7 +92,8 @@ LaunchShape combine_shape(int64_t tokens, int64_t hidden, int vec_elems) {
   const int64_t slots = (tokens + 7) / 8 * 8;
   if (slots <= 0) return LaunchShape{0, 0, block, kCombineU};
   const int64_t g = std::min<int64_t>(chunks, std::max<int64_t>(1, kMaxCombineGrid / slots));
-  return LaunchShape{(int)(slots * g), (int)g, block, kCombineU};
+  const int lds = (block == 64 && chunks >= kCombineCapChunks) ? kCombineCapLds : 0;
+  return LaunchShape{(int)(slots * g), (int)g, block, kCombineU, lds};
 }
 
 // Do the non-NULL entries of p[0..n) lie at base + d * stride?  NULL

@@ -88,6 +88,8 @@ int main() {
     }
     const LaunchShape c = moe_ep_detail::combine_shape(5, nv, 1);
     expect((int64_t)c.grid_y * c.block * c.u >= nv || c.grid_y == moe_ep_detail::kMaxGridY, "combine covers the row");
+    expect(c.lds == ((nv + 63) / 64 >= moe_ep_detail::kCombineCapChunks ? moe_ep_detail::kCombineCapLds : 0),
+           "combine residency cap only on rows of many chunks");
   }
 
   // The copy order AUTO picks: destination-major for groups of at most 16
@@ -151,6 +153,7 @@ int main() {
     const LaunchShape c = moe_ep_detail::combine_shape(tokens, 7168, 8);
     const int64_t slots = (tokens + 7) / 8 * 8;
     expect(c.grid_x == slots * c.grid_y && c.block == moe_ep_detail::kCombineBlock, "combine grid");
+    expect(c.lds == moe_ep_detail::kCombineCapLds && 163840 / c.lds == 18, "combine residency cap on 14 KiB rows");
     expect((int64_t)c.grid_y * c.block >= 7168 / 8, "combine chunks cover the row");
     const moe_ep_detail::OwnerDiv od = moe_ep_detail::make_owner_div((uint32_t)c.grid_y);
     std::vector<int> seen((size_t)slots * c.grid_y, 0);

@@ -186,6 +186,11 @@ struct LaunchShape {
 // asked for but its grid would not fit.
 bool plan_dispatch(DispatchKArgs& a, int vec_bytes, int requested);
 
+// Dynamic LDS bytes to reserve per destination-major workgroup (never
+// touched by the code): a residency cap for the lean instantiation on grids
+// of at least two resident generations, else 0.
+int dispatch_dst_lds(int64_t items, bool lean);
+
 // Enqueue one dispatch kernel (after plan_dispatch).  vec_bytes in
 // {16, 8, 4, 2, 1} must divide hidden_bytes and every hidden row pointer.
 hipError_t launch_dispatch(const DispatchKArgs& a, int vec_bytes, hipStream_t stream);

@@ -815,6 +815,7 @@ hipError_t launch_dispatch(const DispatchKArgs& args, int vec_bytes, hipStream_t
   const bool devn = a.dev_n != nullptr;
   const void* fn;
   dim3 grid, block;
+  size_t lds = 0;
   if (a.order == MOE_EP_ORDER_DESTINATION) {
     if (a.dm_items + extra <= 0) return hipSuccess;
     // top_k <= 64, no scale rows, no statistics rows: the lean instantiation
@@ -822,6 +823,7 @@ hipError_t launch_dispatch(const DispatchKArgs& args, int vec_bytes, hipStream_t
     fn = lean ? pick_kernel<DestinationLeanKernel>(vec_bytes, a.dm_u, devn)
               : pick_kernel<DestinationKernel>(vec_bytes, a.dm_u, devn);
     grid = dim3((unsigned)(a.dm_items + extra));
+    lds = (size_t)dispatch_dst_lds(a.dm_items, lean);
     block = dim3(a.dm_threads);
     a.block = a.dm_threads;
   } else {
@@ -838,7 +840,7 @@ hipError_t launch_dispatch(const DispatchKArgs& args, int vec_bytes, hipStream_t
   uint64_t m_ep = a.div_ep.magic, m_tpr = a.div_tpr.magic;
   uint32_t shifts = a.div_chunks.shift | a.div_block_rows.shift << 8 | a.div_ep.shift << 16 | a.div_tpr.shift << 24;
   void* kargs[] = {&m_chunks, &m_block_rows, &m_ep, &m_tpr, &shifts, &a.dm_chunks, &a.dm_block_rows, &a.ep, &a.tpr, &a};
-  return hipLaunchKernel(fn, grid, block, kargs, 0, stream);
+  return hipLaunchKernel(fn, grid, block, kargs, lds, stream);
 }
 
 hipError_t launch_combine(const CombineKArgs& args, int dtype, int vec_elems, hipStream_t stream) {

@@ -184,4 +184,21 @@ bool plan_dispatch(DispatchKArgs& a, int vec_bytes, int requested) {
   return true;
 }
 
+// Destination-major residency cap: 16 KiB of LDS per workgroup leaves room
+// for 10 workgroups per CU (160 KiB) instead of 16.  In interleaved sweeps
+// (µs per dispatch, uncapped vs capped) it made the lean kernel faster once
+// its grid holds at least 8192 workgroups, two generations of the uncapped
+// residency: 8 ranks x 128 tokens of 14 KiB rows 15.66-15.76 vs 15.44-15.49,
+// of 8 KiB rows (one-wave workgroups) 10.56-10.61 vs 10.10-10.13, 16 x 64
+// 19.35-19.51 vs 19.21-19.24, 4 x 512 1-2% faster; smaller grids were even
+// or slower (16 x 16: 6.69-6.73 vs 6.88).  The kernel with scale rows or
+// statistics rows was 18-25% slower capped (fp8 rows, 8 x 128), and so was
+// the source-row kernel (5-25%), so neither is capped.
+constexpr int64_t kDmCapItems = 8192;
+constexpr int kDmCapLds = 16384;
+
+int dispatch_dst_lds(int64_t items, bool lean) {
+  return lean && items >= kDmCapItems ? kDmCapLds : 0;
+}
+
 }  // namespace moe_ep_detail

@@ -148,6 +148,11 @@ int main() {
     }
   }
 
+  // Destination-major residency cap: lean kernel, grids of 8192+ workgroups.
+  expect(moe_ep_detail::dispatch_dst_lds(8192, true) == 16384 && 163840 / 16384 == 10, "dispatch cap on large grids");
+  expect(moe_ep_detail::dispatch_dst_lds(8191, true) == 0, "no dispatch cap below two generations");
+  expect(moe_ep_detail::dispatch_dst_lds(16384, false) == 0, "no dispatch cap on the full kernel");
+
   // Combine grid: every (token slot, chunk) once, token 8q + x on XCD x.
   for (int64_t tokens : {1, 7, 8, 9, 1000, 1024}) {
     const LaunchShape c = moe_ep_detail::combine_shape(tokens, 7168, 8);

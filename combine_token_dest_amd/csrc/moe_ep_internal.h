@@ -62,13 +62,13 @@ static_assert(sizeof(SourceRank) == 64, "one cache line per source rank");
 
 // Arguments of the dispatch kernels.  The launcher passes the item decode
 // (the div_* constants, the plan values, ep and tpr) as leading scalar
-// kernel arguments, preloaded into registers at wave launch, and this struct
-// by value after them.  Its scalars come first and contiguous, so a
-// workgroup gets the rest of them in one batch of scalar loads, together
-// with its source rank's record (spread over 3 KB of arguments, they had
-// cost each workgroup a chain of dependent scalar-cache round trips before
-// its first data load).
-struct DispatchKArgs {
+// kernel arguments, preloaded into registers at wave launch, and a
+// DispatchArgs<MR> by value after them.  Its scalars come first and
+// contiguous, so a workgroup gets the rest of them in one batch of scalar
+// loads, together with its source rank's record (spread over 3 KB of
+// arguments, they had cost each workgroup a chain of dependent scalar-cache
+// round trips before its first data load).
+struct DispatchArgsHead {
   OwnerDiv div_chunks;                 // destination-major decode: / dm_chunks (set by the launcher)
   OwnerDiv div_block_rows;             //   / dm_block_rows
   OwnerDiv div_ep;                     //   / ep
@@ -82,7 +82,7 @@ struct DispatchKArgs {
   int32_t dm_blocks;                   //   blocks per XCD
   int32_t invalid_id;
   int32_t block;                       // threads per workgroup of the launch (blockDim.x; set by the launcher)
-  int32_t pad0;
+  int32_t grid_y;                      // source-row order: column chunks in the grid (gridDim.y; set by the launcher)
   uint64_t active;                     // active ranks & ((1 << ep) - 1)
   OwnerDiv owner;
   uint8_t* ws;                         // workspace base
@@ -104,15 +104,23 @@ struct DispatchKArgs {
   int64_t off_eplb;
   int64_t eplb_bytes;                  // 0 when no statistics are gathered
   int64_t pad1[6];                     // the per-rank records start on a 64-byte boundary
-  SourceRank src[kMaxRanks];           // per source rank
 };
-static_assert(offsetof(DispatchKArgs, src) % 64 == 0, "per-rank records on 64-byte boundaries");
+static_assert(sizeof(DispatchArgsHead) % 64 == 0, "per-rank records on 64-byte boundaries");
+
+// The head and one record per source rank, for groups of up to MR ranks.
+// The host builds the MR = kMaxRanks form; a group of at most kSmallGroup
+// ranks launches with the kSmallGroup form (see kSmallGroup).
+template <int MR>
+struct DispatchArgs : DispatchArgsHead {
+  SourceRank src[MR];                  // per source rank
+};
+using DispatchKArgs = DispatchArgs<kMaxRanks>;
 
 // Arguments of the combine kernel.  The launcher passes the fields every
 // workgroup needs before its first row load (chunk_div through eo_stride)
-// as leading scalar kernel arguments, preloaded into registers, and the
-// whole struct by value after them for the rest.
-struct CombineKArgs {
+// as leading scalar kernel arguments, preloaded into registers, and a
+// CombineArgs<MR> by value after them for the rest.
+struct CombineArgsHead {
   OwnerDiv chunk_div;                       // workgroup index / 8 / chunks
   int32_t ntok;                             // token slots (slots past it store nothing)
   int32_t chunks;                           // column chunks of a row per token in the grid
@@ -129,10 +137,27 @@ struct CombineKArgs {
   const int32_t* dev_counts;                // counts written by dispatch (device-count steps), else NULL
   OwnerDiv tpr_div;                         // slot / tpr (device-count steps)
   int32_t ep;
-  const uint8_t* expert_output[kMaxRanks];  // per rank d: [ep*tpr, hidden]
-  uint8_t* output[kMaxRanks];               // per source rank s: [n_s, hidden]
-  int32_t token_start[kMaxRanks + 1];       // prefix sums of n_s (host counts)
 };
+
+template <int MR>
+struct CombineArgs : CombineArgsHead {
+  const uint8_t* expert_output[MR];         // per rank d: [ep*tpr, hidden]
+  uint8_t* output[MR];                      // per source rank s: [n_s, hidden]
+  int32_t token_start[MR + 1];              // prefix sums of n_s (host counts)
+};
+using CombineKArgs = CombineArgs<kMaxRanks>;
+
+// Groups of at most kSmallGroup ranks launch with argument blocks sized for
+// kSmallGroup ranks: 888 bytes of kernel arguments for dispatch and 328 for
+// combine, instead of 4472 and 1448.  On this stack a kernel whose arguments
+// fit in 1 KiB starts ~3 us sooner on an idle GPU (launch + synchronise
+// 11.3-11.8 us against 13.0-14.9 us from 1088 bytes up) and costs the host
+// ~0.5-1 us less per launch.  The kernels read no implicit arguments
+// (blockDim and gridDim come in the argument block), which would add 256
+// bytes.
+constexpr int kSmallGroup = 8;
+static_assert(sizeof(DispatchArgs<kSmallGroup>) + 64 <= 1024 && sizeof(CombineArgs<kSmallGroup>) + 64 <= 1024,
+              "the small argument blocks (after at most 64 bytes of leading arguments) fit in 1 KiB");
 
 // Launch configurations, chosen by timing variants on MI355X in the same
 // alternation the bench uses (8 workspaces rotated so the 256 MB MALL holds

@@ -125,8 +125,8 @@ constexpr int kCombineSP = kCpNt;
 // Destination mask of token (s, t): lane j of every wave loads id j, the
 // owner bits are OR-ed across the lanes (a single load for top_k <= 64), and
 // the active-rank mask is applied.  Zero for padding rows.
-__device__ __forceinline__ uint64_t route_token(const DispatchKArgs& a, const int32_t* __restrict__ idr,
-                                                const bool real) {
+template <class A>
+__device__ __forceinline__ uint64_t route_token(const A& a, const int32_t* __restrict__ idr, const bool real) {
   if (!real) return 0;
   const int K = a.top_k;
   const int lane = threadIdx.x & 63;
@@ -150,9 +150,9 @@ __device__ __forceinline__ uint64_t route_token(const DispatchKArgs& a, const in
 // Slot j of receive row r on rank d: the token's id and weight when d
 // receives it, else the invalid id and 0.0.  (Both branches are written out
 // so the compiler does not merge the two sources into one flat load.)
-__device__ __forceinline__ void write_slot(const DispatchKArgs& a, uint8_t* part, const int r, const int j,
-                                           const bool routed, const int32_t* __restrict__ idr,
-                                           const float* __restrict__ wr) {
+template <class A>
+__device__ __forceinline__ void write_slot(const A& a, uint8_t* part, const int r, const int j, const bool routed,
+                                           const int32_t* __restrict__ idr, const float* __restrict__ wr) {
   const int64_t slot = (int64_t)r * a.top_k + j;
   int32_t* ids_out = reinterpret_cast<int32_t*>(part + a.off_ids) + slot;
   float* w_out = reinterpret_cast<float*>(part + a.off_weights) + slot;
@@ -189,8 +189,8 @@ __device__ __forceinline__ int hdiv(uint64_t magic, uint32_t shifts, int which, 
 // when the kernel runs (clamped to the rows the buffers hold) and recorded
 // for combine; else the host's count.  The two are separate instantiations:
 // the run-time test alone cost ~2% on the DeepSeek-V3-shaped dispatch.
-template <bool DEVN>
-__device__ __forceinline__ int step_count(const DispatchKArgs& a, const int s, const bool first, const int tpr) {
+template <bool DEVN, class A>
+__device__ __forceinline__ int step_count(const A& a, const int s, const bool first, const int tpr) {
   if (!DEVN) return a.src[s].n;
   const int c = a.dev_n[s];
   const int ns = c < 0 ? 0 : (c > tpr ? tpr : c);
@@ -198,8 +198,8 @@ __device__ __forceinline__ int step_count(const DispatchKArgs& a, const int s, c
   return ns;
 }
 
-template <int VB, int U, int LP, int SP, bool DEVN>
-__device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const DispatchHead& h, const int r) {
+template <int VB, int U, int LP, int SP, bool DEVN, class A>
+__device__ __forceinline__ void dispatch_row(const A& a, const DispatchHead& h, const int r) {
   typedef typename Bytes<VB>::type V;
   const int s = hdiv(h.m_tpr, h.shifts, 3, r);
   const int t = r - s * h.tpr;
@@ -280,7 +280,7 @@ __device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const Dispa
   // Store each chunk to every destination; further chunks (rows longer than
   // the grid's chunks) are loaded here.
   const int64_t dst_off = a.off_hidden + (int64_t)r * a.hidden_bytes;
-  for (int64_t c0 = c_first; c0 < nv; c0 += (int64_t)gridDim.y * per_block) {
+  for (int64_t c0 = c_first; c0 < nv; c0 += (int64_t)a.grid_y * per_block) {
     if (c0 != c_first) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -304,19 +304,20 @@ __device__ __forceinline__ void dispatch_row(const DispatchKArgs& a, const Dispa
 
 // Gathers source rank s's expert-load statistics into row s of the
 // [ep, eplb_bytes] statistics region of every rank.
-__device__ __forceinline__ void gather_stats_row(const DispatchKArgs& a, const int s) {
+template <class A>
+__device__ __forceinline__ void gather_stats_row(const A& a, const int s) {
   const int64_t B = a.eplb_bytes;
   const int64_t dst_off = a.off_eplb + (int64_t)s * B;
   if (a.eplb_vec4) {
     const uint32_t* src = reinterpret_cast<const uint32_t*>(a.src[s].eplb);
-    for (int64_t c = threadIdx.x; c < B / 4; c += blockDim.x) {
+    for (int64_t c = threadIdx.x; c < B / 4; c += a.block) {
       const uint32_t x = src[c];
       for (int d = 0; d < a.ep; ++d)
         reinterpret_cast<uint32_t*>(a.ws + (int64_t)d * a.part_stride + dst_off)[c] = x;
     }
   } else {
     const uint8_t* src = a.src[s].eplb;
-    for (int64_t c = threadIdx.x; c < B; c += blockDim.x) {
+    for (int64_t c = threadIdx.x; c < B; c += a.block) {
       const uint8_t x = src[c];
       for (int d = 0; d < a.ep; ++d) (a.ws + (int64_t)d * a.part_stride + dst_off)[c] = x;
     }
@@ -342,11 +343,11 @@ __device__ __forceinline__ int source_row_of(const int i, const int rows) {
 // Grid: x = receive row (source_row_of the workgroup index; r = s*tpr + t),
 // then one statistics row per source rank when statistics are gathered;
 // y = column chunk of the hidden row.
-template <int VB, int U, int LP, int SP, bool DEVN>
+template <int VB, int U, int LP, int SP, bool DEVN, int MR>
 __global__ void __launch_bounds__(kMaxBlock)
 dispatch_kernel(const uint64_t m_chunks, const uint64_t m_block_rows, const uint64_t m_ep, const uint64_t m_tpr,
                 const uint32_t shifts, const int32_t dm_chunks, const int32_t dm_block_rows, const int32_t ep,
-                const int32_t tpr, const DispatchKArgs a) {
+                const int32_t tpr, const DispatchArgs<MR> a) {
   // One workgroup per item (no grid-stride loop: a store of one item could
   // then alias the next item's loads, which keeps the compiler from using
   // scalar loads for the uniform ones).
@@ -376,8 +377,8 @@ dispatch_kernel(const uint64_t m_chunks, const uint64_t m_block_rows, const uint
 // rows -- without the loops and branches the general one needs; it took
 // ~0.3 us (1.6%) off the DeepSeek-V3-shaped dispatch in interleaved runs.
 // ---------------------------------------------------------------------------
-template <int VB, int U, int SP, bool DEVN, bool LEAN>
-__device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const DispatchHead& h, const int i) {
+template <int VB, int U, int SP, bool DEVN, bool LEAN, class A>
+__device__ __forceinline__ void dispatch_dst_item(const A& a, const DispatchHead& h, const int i) {
   typedef typename Bytes<VB>::type V;
   // 32-bit decode: the host keeps the item count below 2^31.
   const int rows = h.ep * h.tpr;
@@ -522,11 +523,11 @@ __device__ __forceinline__ void dispatch_dst_item(const DispatchKArgs& a, const 
 
 // Grid: x = destination-major item, then one statistics row per source rank
 // when statistics are gathered.
-template <int VB, int U, int SP, bool DEVN, bool LEAN>
+template <int VB, int U, int SP, bool DEVN, bool LEAN, int MR>
 __global__ void __launch_bounds__(kMaxBlock)
 dispatch_dst_kernel(const uint64_t m_chunks, const uint64_t m_block_rows, const uint64_t m_ep, const uint64_t m_tpr,
                     const uint32_t shifts, const int32_t dm_chunks, const int32_t dm_block_rows, const int32_t ep,
-                    const int32_t tpr, const DispatchKArgs a) {
+                    const int32_t tpr, const DispatchArgs<MR> a) {
   const DispatchHead h{m_chunks, m_block_rows, m_ep, m_tpr, shifts, dm_chunks, dm_block_rows, ep, tpr};
   const int i = blockIdx.x;
   if (LEAN || i < a.dm_items) {
@@ -622,8 +623,8 @@ struct CombineHead {
   int32_t chunks;
 };
 
-template <int DT, int VE, int U, int DB, int LP, int SP, bool ONEPASS, bool STRIDED, bool DEVN>
-__device__ __forceinline__ void combine_token(const CombineKArgs& a, const CombineHead& h, const int b,
+template <int DT, int VE, int U, int DB, int LP, int SP, bool ONEPASS, bool STRIDED, bool DEVN, class A>
+__device__ __forceinline__ void combine_token(const A& a, const CombineHead& h, const int b,
                                               const int chunk, const bool store) {
   typedef typename CVec<DT, VE>::type V;
   int s;
@@ -739,11 +740,11 @@ __device__ __forceinline__ void combine_token(const CombineKArgs& a, const Combi
 // token on one XCD made these small workgroups 5% faster on the
 // DeepSeek-V3-shaped round than one 896-thread workgroup per token; placed
 // round-robin they were no faster.
-template <int DT, int VE, int U, int DB, int LP, int SP, bool ONEPASS, bool STRIDED, bool DEVN>
+template <int DT, int VE, int U, int DB, int LP, int SP, bool ONEPASS, bool STRIDED, bool DEVN, int MR>
 __global__ void __launch_bounds__(kMaxCombineBlock)
 combine_kernel(const uint64_t chunk_magic, const uint32_t chunk_shift, const int32_t ntok, const int32_t chunks,
                const int32_t block, const TokenRec* tokens, const uint8_t* eo_base, const int64_t eo_stride,
-               const int64_t hidden, const CombineKArgs a) {
+               const int64_t hidden, const CombineArgs<MR> a) {
   // One workgroup per item, no grid-stride loop: with stores ahead of it in
   // the same workgroup the token-record load could not be a scalar load.
   // Every test or argument load between the start and the first row load
@@ -762,10 +763,10 @@ combine_kernel(const uint64_t chunk_magic, const uint32_t chunk_shift, const int
   combine_token<DT, VE, U, DB, LP, SP, ONEPASS, STRIDED, DEVN>(a, h, real ? b : ntok - 1, chunk, real);
 }
 
-template <int DT, int VE>
+template <int DT, int VE, int MR>
 const void* pick_combine(bool onepass, bool strided, bool devn) {
 #define MOE_EP_CK(OP, ST, DV) \
-  reinterpret_cast<const void*>(&combine_kernel<DT, VE, kCombineU, kCombineDB, kCombineLP, kCombineSP, OP, ST, DV>)
+  reinterpret_cast<const void*>(&combine_kernel<DT, VE, kCombineU, kCombineDB, kCombineLP, kCombineSP, OP, ST, DV, MR>)
   if (onepass) {
     if (strided) return devn ? MOE_EP_CK(true, true, true) : MOE_EP_CK(true, true, false);
     return devn ? MOE_EP_CK(true, false, true) : MOE_EP_CK(true, false, false);
@@ -795,15 +796,45 @@ const void* pick_kernel(int vec_bytes, int u, bool devn) {
 #undef MOE_EP_PICK
 }
 
-template <int VB, int U, bool DEVN> struct SourceRowKernel {
-  static const void* fn() { return reinterpret_cast<const void*>(&dispatch_kernel<VB, U, kDispatchLP, kDispatchSP, DEVN>); }
+// The dispatch kernels for argument blocks of MR ranks.
+template <int MR> struct DispatchKernels {
+  template <int VB, int U, bool DEVN> struct SourceRow {
+    static const void* fn() {
+      return reinterpret_cast<const void*>(&dispatch_kernel<VB, U, kDispatchLP, kDispatchSP, DEVN, MR>);
+    }
+  };
+  template <int VB, int U, bool DEVN> struct Destination {
+    static const void* fn() {
+      return reinterpret_cast<const void*>(&dispatch_dst_kernel<VB, U, kDispatchSP, DEVN, false, MR>);
+    }
+  };
+  template <int VB, int U, bool DEVN> struct DestinationLean {
+    static const void* fn() {
+      return reinterpret_cast<const void*>(&dispatch_dst_kernel<VB, U, kDispatchSP, DEVN, true, MR>);
+    }
+  };
 };
-template <int VB, int U, bool DEVN> struct DestinationKernel {
-  static const void* fn() { return reinterpret_cast<const void*>(&dispatch_dst_kernel<VB, U, kDispatchSP, DEVN, false>); }
-};
-template <int VB, int U, bool DEVN> struct DestinationLeanKernel {
-  static const void* fn() { return reinterpret_cast<const void*>(&dispatch_dst_kernel<VB, U, kDispatchSP, DEVN, true>); }
-};
+
+// The argument block a group of at most kSmallGroup ranks launches with: the
+// same head and the first kSmallGroup per-rank entries.
+DispatchArgs<kSmallGroup> small_args(const DispatchKArgs& a) {
+  DispatchArgs<kSmallGroup> o;
+  static_cast<DispatchArgsHead&>(o) = a;
+  for (int s = 0; s < kSmallGroup; ++s) o.src[s] = a.src[s];
+  return o;
+}
+
+CombineArgs<kSmallGroup> small_args(const CombineKArgs& a) {
+  CombineArgs<kSmallGroup> o;
+  static_cast<CombineArgsHead&>(o) = a;
+  for (int s = 0; s < kSmallGroup; ++s) {
+    o.expert_output[s] = a.expert_output[s];
+    o.output[s] = a.output[s];
+    o.token_start[s] = a.token_start[s];
+  }
+  o.token_start[kSmallGroup] = a.token_start[kSmallGroup];
+  return o;
+}
 
 hipError_t launch_dispatch(const DispatchKArgs& args, int vec_bytes, hipStream_t stream) {
   DispatchKArgs a = args;
@@ -813,6 +844,7 @@ hipError_t launch_dispatch(const DispatchKArgs& args, int vec_bytes, hipStream_t
   a.div_ep = make_owner_div((uint32_t)std::max(1, a.ep));
   const int64_t extra = a.eplb_bytes ? a.ep : 0;
   const bool devn = a.dev_n != nullptr;
+  const bool small = a.ep <= kSmallGroup;
   const void* fn;
   dim3 grid, block;
   size_t lds = 0;
@@ -820,8 +852,12 @@ hipError_t launch_dispatch(const DispatchKArgs& args, int vec_bytes, hipStream_t
     if (a.dm_items + extra <= 0) return hipSuccess;
     // top_k <= 64, no scale rows, no statistics rows: the lean instantiation
     const bool lean = a.top_k <= 64 && a.scale_bytes == 0 && extra == 0 && a.dm_threads >= 64;
-    fn = lean ? pick_kernel<DestinationLeanKernel>(vec_bytes, a.dm_u, devn)
-              : pick_kernel<DestinationKernel>(vec_bytes, a.dm_u, devn);
+    if (small)
+      fn = lean ? pick_kernel<DispatchKernels<kSmallGroup>::DestinationLean>(vec_bytes, a.dm_u, devn)
+                : pick_kernel<DispatchKernels<kSmallGroup>::Destination>(vec_bytes, a.dm_u, devn);
+    else
+      fn = lean ? pick_kernel<DispatchKernels<kMaxRanks>::DestinationLean>(vec_bytes, a.dm_u, devn)
+                : pick_kernel<DispatchKernels<kMaxRanks>::Destination>(vec_bytes, a.dm_u, devn);
     grid = dim3((unsigned)(a.dm_items + extra));
     lds = (size_t)dispatch_dst_lds(a.dm_items, lean);
     block = dim3(a.dm_threads);
@@ -829,17 +865,22 @@ hipError_t launch_dispatch(const DispatchKArgs& args, int vec_bytes, hipStream_t
   } else {
     const LaunchShape sh = dispatch_shape((int64_t)a.ep * a.tpr + extra, a.hidden_bytes, vec_bytes);
     if (sh.grid_x <= 0) return hipSuccess;
-    fn = pick_kernel<SourceRowKernel>(vec_bytes, sh.u, devn);
+    fn = small ? pick_kernel<DispatchKernels<kSmallGroup>::SourceRow>(vec_bytes, sh.u, devn)
+               : pick_kernel<DispatchKernels<kMaxRanks>::SourceRow>(vec_bytes, sh.u, devn);
     grid = dim3(sh.grid_x, sh.grid_y);
     block = dim3(sh.block);
     a.block = sh.block;
+    a.grid_y = sh.grid_y;
   }
   if (!fn) return hipErrorInvalidValue;
   // The leading arguments (preloaded into scalar registers), then the rest.
   uint64_t m_chunks = a.div_chunks.magic, m_block_rows = a.div_block_rows.magic;
   uint64_t m_ep = a.div_ep.magic, m_tpr = a.div_tpr.magic;
   uint32_t shifts = a.div_chunks.shift | a.div_block_rows.shift << 8 | a.div_ep.shift << 16 | a.div_tpr.shift << 24;
-  void* kargs[] = {&m_chunks, &m_block_rows, &m_ep, &m_tpr, &shifts, &a.dm_chunks, &a.dm_block_rows, &a.ep, &a.tpr, &a};
+  DispatchArgs<kSmallGroup> sa;
+  if (small) sa = small_args(a);
+  void* kargs[] = {&m_chunks, &m_block_rows, &m_ep, &m_tpr, &shifts, &a.dm_chunks, &a.dm_block_rows, &a.ep, &a.tpr,
+                   small ? static_cast<void*>(&sa) : static_cast<void*>(&a)};
   return hipLaunchKernel(fn, grid, block, kargs, lds, stream);
 }
 
@@ -853,11 +894,15 @@ hipError_t launch_combine(const CombineKArgs& args, int dtype, int vec_elems, hi
   const bool onepass = (int64_t)sh.grid_y * sh.block * kCombineU >= a.hidden / vec_elems;
   const bool strided = common_stride(a.expert_output, a.ep, &a.eo_base, &a.eo_stride);
   const bool devn = a.dev_counts != nullptr;
+  const bool small = a.ep <= kSmallGroup;
   a.block = sh.block;
   a.chunk_div = make_owner_div((uint32_t)a.chunks);
   if (devn) a.tpr_div = make_owner_div((uint32_t)a.tpr);
 #define MOE_EP_C(DT, VE) \
-    case VE: fn = pick_combine<DT, VE>(onepass, strided, devn); break;
+    case VE: \
+      fn = small ? pick_combine<DT, VE, kSmallGroup>(onepass, strided, devn) \
+                 : pick_combine<DT, VE, kMaxRanks>(onepass, strided, devn); \
+      break;
   if (dtype == MOE_EP_F32) {
     switch (vec_elems) {
       MOE_EP_C(MOE_EP_F32, 4) MOE_EP_C(MOE_EP_F32, 2) MOE_EP_C(MOE_EP_F32, 1)
@@ -884,7 +929,10 @@ hipError_t launch_combine(const CombineKArgs& args, int dtype, int vec_elems, hi
   const uint8_t* eo_base = a.eo_base;
   int64_t eo_stride = a.eo_stride;
   int64_t hidden = a.hidden;
-  void* kargs[] = {&magic, &shift, &a.ntok, &a.chunks, &a.block, &tokens, &eo_base, &eo_stride, &hidden, &a};
+  CombineArgs<kSmallGroup> sa;
+  if (small) sa = small_args(a);
+  void* kargs[] = {&magic, &shift, &a.ntok, &a.chunks, &a.block, &tokens, &eo_base, &eo_stride, &hidden,
+                   small ? static_cast<void*>(&sa) : static_cast<void*>(&a)};
   return hipLaunchKernel(fn, dim3(sh.grid_x), dim3(sh.block), kargs, (size_t)sh.lds, stream);
 }
 

@@ -137,25 +137,32 @@ def test_graph_replays_ragged_steps_with_device_counts(order):
 
 
 @pytest.mark.parametrize("order", ["source", "destination"])
-def test_device_counts_are_clamped_to_the_buffers(order):
-    """Counts outside [0, tokens_per_rank] are clamped by the kernels."""
-    w = wl.BY_NAME["tiny"]
+@pytest.mark.parametrize("name", ["tiny", "fp8"])
+def test_device_counts_are_clamped_to_the_buffers(name, order):
+    """Counts outside [0, tokens_per_rank] are clamped by the kernels (4
+    ranks, and 16 ranks with scale rows: both sizes of the kernels'
+    argument blocks)."""
+    w = wl.BY_NAME[name]
     cap = w.max_tokens_per_rank
-    log(f"[graph] device counts clamped, {order} order")
+    log(f"[graph] device counts clamped, {name}, {order} order")
     full = parity.case_from_workload(w)
     moe = parity.make_gpu(full, order=order)
-    hid, ids, wts, _ = parity.upload(full)
-    counts = torch.tensor([-3, cap + 100, 5, cap], dtype=torch.int32, device="cuda")
-    res = moe.dispatch(hid, ids, wts, local_num_tokens_device=counts)
-    outs = moe.combine([moe.get_combine_input_buffer(d, torch.float32) for d in range(w.ep_size)])
+    hid, ids, wts, scl = parity.upload(full)
+    dev = ([-3, cap + 100, 5, cap] * w.ep_size)[:w.ep_size]
+    counts = torch.tensor(dev, dtype=torch.int32, device="cuda")
+    res = moe.dispatch(hid, ids, wts, hidden_states_scale=scl, local_num_tokens_device=counts)
+    cdt = torch.float32 if w.combine_dtype == "f32" else torch.bfloat16
+    outs = moe.combine([moe.get_combine_input_buffer(d, cdt) for d in range(w.ep_size)])
     torch.cuda.synchronize()
-    nt = [0, cap, 5, cap]
+    nt = [min(max(x, 0), cap) for x in dev]
     c = parity.case_from_workload(w)
     c.hidden = [h[:n] for h, n in zip(c.hidden, nt)]
     c.ids = [x[:n] for x, n in zip(c.ids, nt)]
     c.weights = [x[:n] for x, n in zip(c.weights, nt)]
+    if c.scale is not None:
+        c.scale = [x[:n] for x, n in zip(c.scale, nt)]
     om = oracle.OracleMoEEp(parity.oracle_params(c))
-    ores = om.dispatch(c.hidden, c.ids, c.weights, runtime_max_tokens_per_rank=cap)
+    ores = om.dispatch(c.hidden, c.ids, c.weights, hidden_states_scale=c.scale, runtime_max_tokens_per_rank=cap)
     parity.compare_dispatch(c, res, ores, "clamped")
     assert [tuple(o.shape) for o in outs] == [(cap, w.hidden_size)] * w.ep_size
     moe.destroy()

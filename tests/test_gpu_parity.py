@@ -231,6 +231,14 @@ EDGE = [
     ("eplb_all_empty_rtpr0", dict(ep=4, E=8, K=2, cap=6, n=[0, 0, 0, 0], hidden_size=16, H=32, rtpr=0, eplb=40)),
     ("eplb_mask", dict(ep=8, E=64, K=6, cap=40, n=[40, 39, 0, 1, 2, 40, 13, 7], hidden_size=512, H=1024,
                        mask=0b10110101, eplb=256)),
+    # the kernels' argument blocks hold 8 ranks up to ep = 8 and 64 above:
+    # the last rank's rows, records and statistics on each side of the switch
+    ("ep8_last_rank_block", dict(ep=8, E=32, K=5, cap=24, n=[3, 0, 24, 9, 1, 0, 17, 24], hidden_size=256,
+                                 H=512, S=36, eplb=40, mask=0b11011111)),
+    ("ep9_first_large_block", dict(ep=9, E=36, K=5, cap=24, n=[3, 0, 24, 9, 1, 0, 17, 24, 11], hidden_size=256,
+                                   H=512, S=36, eplb=40, mask=0b110111111)),
+    ("ep9_f16_rtpr", dict(ep=9, E=18, K=3, cap=20, n=[20, 4, 0, 7, 20, 1, 0, 3, 19], hidden_size=100, H=200,
+                          rtpr=20, dtype="f16")),
 ]
 
 

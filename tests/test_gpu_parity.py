@@ -277,8 +277,8 @@ def random_small_config(seed):
 
 
 def test_random_small_configs():
-    """40 seeded random steps, both dispatch orders, against the oracle."""
-    for seed in range(40):
+    """120 seeded random steps, both dispatch orders, against the oracle."""
+    for seed in range(120):
         kw = random_small_config(seed)
         c = random_case(7000 + seed, name=f"random{seed}", **kw)
         for order in ORDERS:
@@ -307,8 +307,8 @@ def random_larger_config(seed):
 
 
 def test_random_larger_configs():
-    """30 seeded random steps with model-sized rows, both dispatch orders."""
-    for seed in range(30):
+    """60 seeded random steps with model-sized rows, both dispatch orders."""
+    for seed in range(60):
         kw = random_larger_config(seed)
         c = random_case(8000 + seed, name=f"larger{seed}", **kw)
         for order in ORDERS:

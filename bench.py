@@ -361,9 +361,10 @@ def main():
                     help="(default) time a plain 1 GiB device-to-device copy: the PMC byte scale, and the "
                          "measured copy bandwidth the round is compared with")
     ap.add_argument("--no-copy-calibration", action="store_true", help="skip the 1 GiB copy")
-    ap.add_argument("--no-two-streams", action="store_true",
-                    help="skip the pass that runs alternate instances' rounds on two streams (profiled "
-                         "runs skip it, with the graph replays)")
+    ap.add_argument("--two-streams", action="store_true",
+                    help="also time the rounds as two overlapping streams of work (off by default: their "
+                         "overlapped launches would enter a kernel trace's per-kernel averages)")
+    ap.add_argument("--no-two-streams", action="store_true", help="(default) skip the two-stream pass")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP graph replays after the timed passes (profiled runs: the kernel "
                          "trace then holds only the set-up, warm-up and timed launches)")
@@ -553,7 +554,7 @@ def main():
     # one stream's kernel ramps and tails overlap the other's.  Reported
     # beside `value`, which stays the one-stream round.
     two_stream_us = None
-    if not args.no_two_streams and I >= 2:
+    if args.two_streams and not args.no_two_streams and I >= 2:
         streams = [torch.cuda.Stream(device), torch.cuda.Stream(device)]     # default priority
         def two_stream_rounds(n):
             for i in range(n):

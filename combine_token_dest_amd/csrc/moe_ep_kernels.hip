@@ -86,6 +86,14 @@ __device__ __forceinline__ typename Bytes<VB>::type buf_load(__amdgpu_buffer_rsr
   }
 }
 
+// The same load through a plain global address (GL rows in combine).
+template <int VB, int CP>
+__device__ __forceinline__ typename Bytes<VB>::type glob_load(const uint8_t* p) {
+  typedef typename Bytes<VB>::type V;
+  if constexpr (CP == kCpNt) return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+  else return *reinterpret_cast<const V*>(p);
+}
+
 template <int VB, int CP>
 __device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, int off, const typename Bytes<VB>::type& v) {
   if constexpr (VB == 16) {
@@ -623,7 +631,7 @@ struct CombineHead {
   int32_t chunks;
 };
 
-template <int DT, int VE, int U, int DB, int LP, int SP, bool ONEPASS, bool STRIDED, bool DEVN, class A>
+template <int DT, int VE, int U, int DB, int LP, int SP, bool ONEPASS, bool STRIDED, bool DEVN, bool GL, class A>
 __device__ __forceinline__ void combine_token(const A& a, const CombineHead& h, const int b,
                                               const int chunk, const bool store) {
   typedef typename CVec<DT, VE>::type V;
@@ -677,29 +685,53 @@ __device__ __forceinline__ void combine_token(const A& a, const CombineHead& h, 
     // and add +0.0.
     auto batch = [&](auto dbx) {
       constexpr int DBX = decltype(dbx)::value;
-      // Every slot starts as a size-0 resource (its loads return 0 and touch
-      // no memory), so no path can load through an unset one.
-      __amdgpu_buffer_rsrc_t rows[DBX];
-#pragma unroll
-      for (int k = 0; k < DBX; ++k) rows[k] = row_rsrc(h.eo_base, 0);
-      int cnt = 0;
-#pragma unroll
-      for (int k = 0; k < DBX; ++k) {
-        if (mm) {
-          const int d = __builtin_ctzll(mm);
-          mm &= mm - 1;
-          const uint8_t* eo = STRIDED ? h.eo_base + (int64_t)d * h.eo_stride : a.expert_output[d];
-          rows[k] = row_rsrc(eo + r * row_bytes, row_bytes);
-          cnt = k + 1;
-        } else if (k > 0) {
-          rows[k] = rows[k - 1];
-        }
-      }
       V v[DBX][U];
+      int cnt = 0;
+      if constexpr (GL) {
+        // Plain global addresses.  A batch with no row left loads nothing
+        // (the call sites never make one), so slot 0 is always a routed row
+        // and every other slot is a routed row or a copy of the one before.
+        if (mm == 0) return;
+        const uint8_t* rows[DBX];
 #pragma unroll
-      for (int k = 0; k < DBX; ++k)
+        for (int k = 0; k < DBX; ++k) {
+          if (mm) {
+            const int d = __builtin_ctzll(mm);
+            mm &= mm - 1;
+            const uint8_t* eo = STRIDED ? h.eo_base + (int64_t)d * h.eo_stride : a.expert_output[d];
+            rows[k] = eo + r * row_bytes;
+            cnt = k + 1;
+          } else {
+            rows[k] = rows[k > 0 ? k - 1 : 0];
+          }
+        }
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[k][u] = buf_load<VB, LP>(rows[k], off[u]);
+        for (int k = 0; k < DBX; ++k)
+#pragma unroll
+          for (int u = 0; u < U; ++u) v[k][u] = glob_load<VB, LP>(rows[k] + off[u]);
+      } else {
+        // Every slot starts as a size-0 resource (its loads return 0 and
+        // touch no memory), so no path can load through an unset one.
+        __amdgpu_buffer_rsrc_t rows[DBX];
+#pragma unroll
+        for (int k = 0; k < DBX; ++k) rows[k] = row_rsrc(h.eo_base, 0);
+#pragma unroll
+        for (int k = 0; k < DBX; ++k) {
+          if (mm) {
+            const int d = __builtin_ctzll(mm);
+            mm &= mm - 1;
+            const uint8_t* eo = STRIDED ? h.eo_base + (int64_t)d * h.eo_stride : a.expert_output[d];
+            rows[k] = row_rsrc(eo + r * row_bytes, row_bytes);
+            cnt = k + 1;
+          } else if (k > 0) {
+            rows[k] = rows[k - 1];
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < DBX; ++k)
+#pragma unroll
+          for (int u = 0; u < U; ++u) v[k][u] = buf_load<VB, LP>(rows[k], off[u]);
+      }
 #pragma unroll
       for (int k = 0; k < DBX; ++k)
 #pragma unroll
@@ -760,7 +792,14 @@ combine_kernel(const uint64_t chunk_magic, const uint32_t chunk_shift, const int
   const int b = q * 8 + (i & 7);
   const bool real = b < ntok;
   const CombineHead h{tokens, eo_base, eo_stride, hidden, block, chunks};
-  combine_token<DT, VE, U, DB, LP, SP, ONEPASS, STRIDED, DEVN>(a, h, real ? b : ntok - 1, chunk, real);
+  // Row loads: through plain global addresses for groups of up to
+  // kSmallGroup ranks, through one buffer resource per row above that.  In
+  // interleaved runs the global loads made the DeepSeek-V3 round's combine
+  // 1.1% faster (16.54 against 16.71-16.76 us, two boxes) and a ragged
+  // 8-rank one 0.6%, but a 32-rank round's 3% slower (95.1-95.4 against
+  // 92.4-93.0 us); a 16-rank fp8 one was even.
+  combine_token<DT, VE, U, DB, LP, SP, ONEPASS, STRIDED, DEVN, (MR <= kSmallGroup)>(a, h, real ? b : ntok - 1, chunk,
+                                                                                   real);
 }
 
 template <int DT, int VE, int MR>

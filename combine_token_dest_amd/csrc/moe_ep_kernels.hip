@@ -692,17 +692,22 @@ __device__ __forceinline__ void combine_token(const A& a, const CombineHead& h, 
         // (the call sites never make one), so slot 0 is always a routed row
         // and every other slot is a routed row or a copy of the one before.
         if (mm == 0) return;
+        auto row_of = [&](const int d) {
+          const uint8_t* eo = STRIDED ? h.eo_base + (int64_t)d * h.eo_stride : a.expert_output[d];
+          return eo + r * row_bytes;
+        };
         const uint8_t* rows[DBX];
+        rows[0] = row_of(__builtin_ctzll(mm));
+        mm &= mm - 1;
+        cnt = 1;
 #pragma unroll
-        for (int k = 0; k < DBX; ++k) {
+        for (int k = 1; k < DBX; ++k) {
           if (mm) {
-            const int d = __builtin_ctzll(mm);
+            rows[k] = row_of(__builtin_ctzll(mm));
             mm &= mm - 1;
-            const uint8_t* eo = STRIDED ? h.eo_base + (int64_t)d * h.eo_stride : a.expert_output[d];
-            rows[k] = eo + r * row_bytes;
             cnt = k + 1;
           } else {
-            rows[k] = rows[k > 0 ? k - 1 : 0];
+            rows[k] = rows[k - 1];
           }
         }
 #pragma unroll

@@ -470,24 +470,32 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall_s = t1 - t0
-    log(f"[bench] then warmup {args.warmup} and timing {K} steps")
     torch.cuda._sleep(spin_cycles)
     hev.record(ea, sp)
     for i in range(KP):
         insts[i % I].dispatch(sp)
         insts[i % I].combine(sp)
     hev.record(eb, sp)
+    torch.cuda.synchronize()
+    round_ms = hev.elapsed_ms(ea, eb) / KP
+    td = np.array([hev.elapsed_ms(ev[g][0], ev[g][1]) for g in range(G)])
+    tc = np.array([hev.elapsed_ms(ev[g][1], ev[g][2]) for g in range(G)])
+    w_g = np.array(sizes, dtype=float)
+    d_ms, c_ms, marker_ms = solve_kernel_times(td, tc, w_g, round_ms)
+    # The events go before the timed steps: with ~60 of them still alive,
+    # launches at decode sizes (host-bound) cost ~1 us more each.
+    for e in ev + [[ea, eb]]:
+        for x in e:
+            hev.destroy(x)
 
     # W untimed warm-up steps, then the timed region: K steps without
     # events, alternating dispatch and combine per instance as a caller
     # would, bracketed by synchronizations: this pass gives the step time and
     # `value` (the passes above attribute time to each kernel).  The warm-up
-    # is queued right behind the alternating pass and the timed steps follow
-    # its synchronisation, so the part is busy up to the timed region: after
-    # 1-100 ms of idle GPU (host work such as the event solve below, which
-    # therefore comes after the timed region) a 20-step region measured
-    # ~0.2-0.5 us per step slower than one started on a part that had just
-    # been busy.
+    # sits right before the timed steps: after 1-100 ms of idle GPU (host
+    # work such as the solve above) a 20-step region measured 0.2-0.5 us per
+    # step slower than one started on a part that had just been busy.
+    log(f"[bench] warmup {args.warmup}, then timing {K} steps")
     for i in range(args.warmup):
         insts[i % I].dispatch(sp)
         insts[i % I].combine(sp)
@@ -498,15 +506,6 @@ def main():
         insts[i % I].combine(sp)
     torch.cuda.synchronize()
     wall_plain = time.perf_counter() - t2
-
-    round_ms = hev.elapsed_ms(ea, eb) / KP
-    td = np.array([hev.elapsed_ms(ev[g][0], ev[g][1]) for g in range(G)])
-    tc = np.array([hev.elapsed_ms(ev[g][1], ev[g][2]) for g in range(G)])
-    w_g = np.array(sizes, dtype=float)
-    d_ms, c_ms, marker_ms = solve_kernel_times(td, tc, w_g, round_ms)
-    for e in ev + [[ea, eb]]:
-        for x in e:
-            hev.destroy(x)
 
     # The same rounds replayed from HIP graphs (one captured dispatch +
     # combine per instance): what a caller that captures the round sees.

@@ -128,8 +128,8 @@ bool common_stride(const uint8_t* const* p, int n, const uint8_t** base, int64_t
 // them.  It launches one workgroup per (destination, row); AUTO takes it for
 // groups of at most 16 ranks with ep * ep * tpr <= 16384 while the
 // source-row grid alone (one workgroup per row) does not fill the chip, and
-// the source-row order otherwise.  Measured with the current kernels (µs
-// per dispatch, source-row vs destination-major, one box):
+// the source-row order otherwise.  Measured before the residency cap below
+// (µs per dispatch, source-row vs destination-major, one box):
 //   14 KiB rows, 8 ranks: 1 token per rank 5.10 vs 4.34, 4: 5.58 vs 4.47,
 //   16: 5.96 vs 5.09, 32: 7.18 vs 6.63, 64: 10.62 vs 10.44, 128: 18.58 vs
 //   16.75, 256: 36.76 vs 36.04;  4 ranks: 16: 5.35 vs 4.51, 64: 6.19 vs
@@ -144,10 +144,27 @@ bool common_stride(const uint8_t* const* p, int n, const uint8_t** base, int64_t
 // of many ranks).  An earlier version of this kernel, whose workgroups
 // waited on a longer chain of argument loads, also needed two resident
 // generations of workgroups to win.
+// Past those bounds, groups of at most 8 ranks whose rows are nearly all
+// real tokens (at least kDmAutoMinFill of ep * tpr, host counts) also take
+// the destination-major order: with the residency cap it won at nearly every
+// such step measured (µs per dispatch, source-row vs destination-major; 14 KiB
+// rows unless noted): 8 x 512 73.9 vs 72.4, 8 x 768 114.6 vs 107.0,
+// 8 x 1024 154.1 vs 141.3, 8 x 2048 306.9 vs 276.5; 8 KiB rows 8 x 512
+// 42.6 vs 33.0, 8 x 1024 86.3 vs 82.2; 16 KiB 8 x 1024 176.6 vs 154.4;
+// 12 KiB 8 x 1024 129.7 vs 122.1; 6 x 512 48.3 vs 37.1, 6 x 1024 101.8 vs
+// 93.7; 4 x 2048 105.6 vs 98.1 (8 KiB 60.5 vs 58.1); fp8 rows with scales
+// 8 x 512 38.4 vs 31.0; except 4 x 1024 of 8 KiB rows (30.0 vs 30.8) and
+// 2 x 2048 (32.0 vs 32.7).  With fewer real rows it loses: 8 x 1024 with
+// each rank 60% full 93.8 vs 101.9 (75%: even, 90%: 140.8 vs 131.7), and
+// ragged counts (U[0, cap], ~40% of the rows) 63.8 vs 74.3 at 8 x 1024 and
+// 17.4 vs 20.8 at 8 x 512 of 8 KiB rows.  Device-count steps, whose counts
+// the host does not know, keep the bounds above.
 constexpr int64_t kDmBlockBytes = 512 * 1024;
 constexpr int64_t kDmXcdRows = 4;            // the kernels' kXcdRows
 constexpr int64_t kDmAutoMaxPairs = 16384;   // ep * ep * tpr
 constexpr int kDmAutoMaxRanks = 16;
+constexpr int kDmAutoFullMaxRanks = 8;
+constexpr double kDmAutoMinFill = 0.8;
 
 bool plan_dispatch(DispatchKArgs& a, int vec_bytes, int requested) {
   const int64_t rows = (int64_t)a.ep * a.tpr;
@@ -155,7 +172,11 @@ bool plan_dispatch(DispatchKArgs& a, int vec_bytes, int requested) {
   a.order = MOE_EP_ORDER_SOURCE_ROW;
   a.dm_items = 0;
   if (requested == MOE_EP_ORDER_SOURCE_ROW) return true;
-  if (automatic && (a.ep > kDmAutoMaxRanks || rows * a.ep > kDmAutoMaxPairs)) return true;
+  int64_t real_rows = 0;
+  for (int s = 0; s < a.ep; ++s) real_rows += a.src[s].n;
+  const bool full_small_group = a.dev_n == nullptr && a.ep <= kDmAutoFullMaxRanks && rows > 0 &&
+                                (double)real_rows >= kDmAutoMinFill * (double)rows;
+  if (automatic && !full_small_group && (a.ep > kDmAutoMaxRanks || rows * a.ep > kDmAutoMaxPairs)) return true;
   // Rows per XCD (the kernel hands rows to the XCDs in blocks of
   // kDmXcdRows), and rows per XCD block, a multiple of kDmXcdRows.
   const int64_t rmax = (rows + 8 * kDmXcdRows - 1) / (8 * kDmXcdRows) * kDmXcdRows;
@@ -170,7 +191,7 @@ bool plan_dispatch(DispatchKArgs& a, int vec_bytes, int requested) {
   const double est = 8.0 * (double)nq * a.ep * (double)b * (double)chunks;
   if (est + a.ep > 2147483647.0) return automatic;     // AUTO falls back to the source-row order
   const int64_t items = 8 * nq * a.ep * b * chunks;
-  if (automatic) {
+  if (automatic && !full_small_group) {
     const LaunchShape src = dispatch_shape(rows, a.hidden_bytes, vec_bytes);
     if (rows >= kResidentWaves / ((src.block + 63) / 64)) return true;    // the source-row grid fills the chip
   }

@@ -95,7 +95,9 @@ int main() {
   // The copy order AUTO picks: destination-major for groups of at most 16
   // ranks with ep * ep * tpr <= 16384 while the source rows alone do not
   // fill the chip; else source-row.
-  struct OrderCase { int ep, tpr; int64_t row_bytes; int requested, expect; };
+  // fill: percent of each rank's tpr rows that are real tokens (host counts);
+  // devn: counts come from device memory.
+  struct OrderCase { int ep, tpr; int64_t row_bytes; int requested, expect; int fill = 0; bool devn = false; };
   const OrderCase order_cases[] = {
       {8, 128, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION},    // DeepSeek-V3 decode round
       {8, 256, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION},
@@ -118,6 +120,16 @@ int main() {
       {4, 16, 512, MOE_EP_ORDER_DESTINATION, MOE_EP_ORDER_DESTINATION},
       {8, 0, 14336, MOE_EP_ORDER_DESTINATION, MOE_EP_ORDER_DESTINATION},
       {8, 128, 14336, MOE_EP_ORDER_SOURCE_ROW, MOE_EP_ORDER_SOURCE_ROW},
+      // groups of at most 8 ranks with at least 80% real rows: destination-major past the bounds
+      {8, 512, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION, 100},
+      {8, 2048, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION, 100},
+      {8, 1024, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION, 81},
+      {8, 1024, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW, 75},
+      {8, 1024, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW, 100, true},   // device counts
+      {4, 1024, 14336, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION, 100},
+      {8, 512, 7168, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_DESTINATION, 100},
+      {16, 256, 7168, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW, 100},          // more than 8 ranks
+      {8, 445, 8192, MOE_EP_ORDER_AUTO, MOE_EP_ORDER_SOURCE_ROW, 42},            // the ragged step's fill
   };
   for (const OrderCase& oc : order_cases) {
     moe_ep_detail::DispatchKArgs k;
@@ -125,6 +137,9 @@ int main() {
     k.ep = oc.ep;
     k.tpr = oc.tpr;
     k.hidden_bytes = oc.row_bytes;
+    for (int s = 0; s < oc.ep; ++s) k.src[s].n = (int32_t)((int64_t)oc.tpr * oc.fill / 100);
+    static const int32_t dev_counts_stand_in = 0;
+    if (oc.devn) k.dev_n = &dev_counts_stand_in;
     expect(moe_ep_detail::plan_dispatch(k, 16, oc.requested), "plan_dispatch");
     expect(k.order == oc.expect, "dispatch order");
     if (k.order == MOE_EP_ORDER_DESTINATION) {

@@ -57,7 +57,8 @@ class _DeviceBytes:
 
 
 def _dev_ptr(t: torch.Tensor, device: torch.device, what: str) -> int:
-    if t.device != device:
+    # get_device() is the cheap form of the device check (-1 for CPU tensors)
+    if t.get_device() != device.index or not t.is_cuda:
         raise ValueError(f"{what} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
@@ -107,6 +108,7 @@ class MoEEp:
             self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
             self._handle = _lib.moe_ep_create(self.params, self.workspace.data_ptr(), nbytes)
         self._ws_base = self.workspace.data_ptr()
+        self._views = {}
         self.last_dispatch_order = None
         self._tpr = None
         self._n = None
@@ -130,10 +132,18 @@ class MoEEp:
         return self.params.ep_size
 
     def _view(self, ptr: int, rows: int, row_bytes: int, dtype: torch.dtype) -> torch.Tensor:
-        off = ptr - self._ws_base
-        flat = self.workspace[off:off + rows * row_bytes]
-        item = torch.empty((), dtype=dtype).element_size()
-        return flat.view(dtype).view(rows, row_bytes // item)
+        # Views of the workspace, kept per (address, shape, dtype): the
+        # layout is fixed for the handle, and building torch views cost most
+        # of a decode-size round's host time.
+        key = (ptr, rows, row_bytes, dtype)
+        v = self._views.get(key)
+        if v is None:
+            off = ptr - self._ws_base
+            v = self.workspace[off:off + rows * row_bytes].view(dtype).view(rows, row_bytes // dtype.itemsize)
+            if len(self._views) > 4096:
+                self._views.clear()
+            self._views[key] = v
+        return v
 
     def dispatch(self, hidden_states: Sequence[torch.Tensor], topk_ids: Sequence[torch.Tensor],
                  topk_weights: Optional[Sequence[Optional[torch.Tensor]]] = None, *,
@@ -161,6 +171,9 @@ class MoEEp:
         if len(hidden_states) != ep or len(topk_ids) != ep:
             raise ValueError(f"expected {ep} per-rank hidden_states and topk_ids")
         a = _lib.moe_ep_dispatch_args()
+        # the struct's array fields, fetched once (each field access builds a new proxy)
+        a_n, a_hidden, a_ids, a_w, a_scale = (a.local_num_tokens, a.hidden, a.topk_ids, a.topk_weights,
+                                             a.hidden_scale)
         wp = sp = 0
         n = []
         keep = []              # int32 copies of int64 ids, alive until the call returns
@@ -178,22 +191,22 @@ class MoEEp:
             if h.shape[0] != ns or h.numel() * h.element_size() != ns * p.hidden_row_bytes:
                 raise ValueError(f"rank {s}: hidden_states must be {ns} rows of {p.hidden_row_bytes} bytes")
             n.append(ns)
-            a.local_num_tokens[s] = ns
-            a.hidden[s] = _dev_ptr(h, self.device, f"hidden_states[{s}]") if ns else None
-            a.topk_ids[s] = _dev_ptr(ids, self.device, f"topk_ids[{s}]") if ns else None
+            a_n[s] = ns
+            a_hidden[s] = _dev_ptr(h, self.device, f"hidden_states[{s}]") if ns else None
+            a_ids[s] = _dev_ptr(ids, self.device, f"topk_ids[{s}]") if ns else None
             if topk_weights is not None and topk_weights[s] is not None:
                 w = topk_weights[s]
                 if w.dtype != torch.float32 or tuple(w.shape) != (ns, p.top_k):
                     raise ValueError(f"rank {s}: topk_weights must be float32 [{ns}, {p.top_k}]")
                 wp |= 1 << s
-                a.topk_weights[s] = _dev_ptr(w, self.device, f"topk_weights[{s}]") if ns else None
+                a_w[s] = _dev_ptr(w, self.device, f"topk_weights[{s}]") if ns else None
             if hidden_states_scale is not None and hidden_states_scale[s] is not None:
                 sc = hidden_states_scale[s]
                 if sc.shape[0] != ns or sc.numel() * sc.element_size() != ns * p.scale_row_bytes:
                     raise ValueError(f"rank {s}: hidden_states_scale must be {ns} rows of "
                                      f"{p.scale_row_bytes} bytes")
                 sp |= 1 << s
-                a.hidden_scale[s] = _dev_ptr(sc, self.device, f"hidden_states_scale[{s}]") if ns else None
+                a_scale[s] = _dev_ptr(sc, self.device, f"hidden_states_scale[{s}]") if ns else None
         ep_present = 0
         if eplb_local_stats is not None:
             if len(eplb_local_stats) != ep:
@@ -258,8 +271,7 @@ class MoEEp:
             raise TypeError(f"combine dtype must be float32, bfloat16 or float16, got {dtype}")
         ptr = _lib.moe_ep_get_combine_input_buffer(self._handle, rank, _COMBINE_DTYPES[dtype])
         self._buffer_dtype = dtype
-        item = torch.empty((), dtype=dtype).element_size()
-        return self._view(ptr, self.params.ep_size * self._tpr, self.params.hidden_size * item, dtype)
+        return self._view(ptr, self.params.ep_size * self._tpr, self.params.hidden_size * dtype.itemsize, dtype)
 
     def combine(self, expert_output: Sequence[Optional[torch.Tensor]], *,
                 output: Optional[Sequence[Optional[torch.Tensor]]] = None,
@@ -288,14 +300,15 @@ class MoEEp:
             raise _lib.MoeEpError(_lib.MOE_EP_ERR_STATE, "combine", "no dispatch to combine")
         rows = ep * self._tpr
         a = _lib.moe_ep_combine_args()
+        a_eo, a_out = a.expert_output, a.output
         for d in range(ep):
             t = expert_output[d]
             if t is None:
-                a.expert_output[d] = None
+                a_eo[d] = None
                 continue
             if t.dtype != dtype or t.numel() != rows * p.hidden_size:
                 raise ValueError(f"rank {d}: expert_output must be {dtype} [{rows}, {p.hidden_size}]")
-            a.expert_output[d] = _dev_ptr(t, self.device, f"expert_output[{d}]")
+            a_eo[d] = _dev_ptr(t, self.device, f"expert_output[{d}]")
         outs = []
         for s in range(ep):
             ns = self._n[s]
@@ -304,7 +317,7 @@ class MoEEp:
                 o = torch.empty((ns, p.hidden_size), dtype=dtype, device=self.device)
             elif o.dtype != dtype or tuple(o.shape) != (ns, p.hidden_size):
                 raise ValueError(f"rank {s}: output must be {dtype} [{ns}, {p.hidden_size}]")
-            a.output[s] = _dev_ptr(o, self.device, f"output[{s}]") if ns else None
+            a_out[s] = _dev_ptr(o, self.device, f"output[{s}]") if ns else None
             outs.append(o)
         a.dtype = _COMBINE_DTYPES[dtype]
         a.active_rank_mask = _mask_value(active_rank_mask)

@@ -74,11 +74,12 @@ typedef enum moe_ep_status {
  *               as one sequential sweep (best for small groups whose
  *               (destination, row) workgroups fill the chip several times).
  *  AUTO:        DESTINATION when ep_size <= 16, ep_size^2 * tokens_per_rank
- *               <= 16384, the destination-major grid holds at least twice
- *               as many workgroups as MI355X runs at once (256 CUs x 32 waves,
- *               two waves per workgroup for 14 KiB rows: 8192), and the
- *               ep_size * tokens_per_rank source rows do not fill the chip
- *               on their own; else SOURCE_ROW.
+ *               <= 16384 and the ep_size * tokens_per_rank source rows do
+ *               not fill the chip on their own (MI355X runs 256 CUs x 32
+ *               waves at once); also when ep_size <= 8 and at least 80% of
+ *               the ep_size * tokens_per_rank rows are real tokens (host
+ *               counts only: a step with device-resident counts uses the
+ *               first rule); else SOURCE_ROW.
  * An explicit DESTINATION request whose grid would pass 2^31 - 1 workgroups
  * makes moe_ep_dispatch fail with MOE_EP_ERR_INVALID_ARG (nothing launched);
  * AUTO then takes SOURCE_ROW instead. */

@@ -71,8 +71,8 @@ typedef enum moe_ep_status {
  *  DESTINATION: a workgroup writes one (destination, row) pair; rows are
  *               pinned to XCDs so the other destinations' re-reads of a row
  *               hit that XCD's L2, and each destination's region is written
- *               as one sequential sweep (best for small groups whose
- *               (destination, row) workgroups fill the chip several times).
+ *               as one sequential sweep (best for groups of a few ranks
+ *               whose rows are mostly real tokens).
  *  AUTO:        DESTINATION when ep_size <= 16, ep_size^2 * tokens_per_rank
  *               <= 16384 and the ep_size * tokens_per_rank source rows do
  *               not fill the chip on their own (MI355X runs 256 CUs x 32

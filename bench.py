@@ -482,8 +482,10 @@ def main():
     tc = np.array([hev.elapsed_ms(ev[g][1], ev[g][2]) for g in range(G)])
     w_g = np.array(sizes, dtype=float)
     d_ms, c_ms, marker_ms = solve_kernel_times(td, tc, w_g, round_ms)
-    # The events go before the timed steps: with ~60 of them still alive,
-    # launches at decode sizes (host-bound) cost ~1 us more each.
+    # The events go before the timed steps: while timing events are alive
+    # (even just two), launches cost more: decode-size rounds measured
+    # 9.2-9.5 instead of 7.6-7.8 us and a 20-step DSv3 region 0.7-0.8 us per
+    # step slower.
     for e in ev + [[ea, eb]]:
         for x in e:
             hev.destroy(x)

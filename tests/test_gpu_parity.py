@@ -93,6 +93,21 @@ def test_auto_order_choice(name, expect):
     moe.destroy()
 
 
+@pytest.mark.parametrize("fill,expect", [(512, "destination"), (410, "destination"), (307, "source")])
+def test_auto_order_at_prefill_capacity(fill, expect):
+    """Past the ep^2 * tokens_per_rank bound (8 ranks x 512 tokens of 14 KiB
+    rows), AUTO takes the destination-major order only when at least 80% of
+    the rows are real tokens (host counts); either way the step is bit-exact,
+    with combine under its residency cap (rows of 14 chunks)."""
+    w = dataclasses.replace(wl.BY_NAME["dsv3"], max_tokens_per_rank=512)
+    c = parity.case_from_workload(w, local_num_tokens=[fill] * 8, seed=9512 + fill)
+    log(f"[parity] dsv3 shape tpr 512, {fill} tokens per rank, auto order")
+    moe = parity.make_gpu(c)
+    parity.run_step(c, moe=moe)
+    assert moe.last_dispatch_order == expect
+    moe.destroy()
+
+
 def test_dsv3_with_expert_load_statistics():
     """The DeepSeek-V3-shaped round with int32 [256] per-rank statistics gathered."""
     w = wl.BY_NAME["dsv3"]

@@ -61,7 +61,8 @@ typedef enum moe_ep_status {
   MOE_EP_ERR_MASK = -4,         /* mask without enable_rank_mask, bits >= ep_size, or combine mask != dispatch mask */
   MOE_EP_ERR_ALIGN = -5,        /* an int32/float/workspace pointer not aligned to its element */
   MOE_EP_ERR_HIP = -6,          /* a HIP runtime call failed (launch or device query) */
-  MOE_EP_ERR_UNSUPPORTED = -7   /* not a gfx950 device */
+  MOE_EP_ERR_UNSUPPORTED = -7   /* no virtual memory management on the device, or a checkpoint
+                                   call on a handle whose workspace the caller owns */
 } moe_ep_status;
 
 /* Order in which dispatch writes the receive rows (moe_ep_params.dispatch_order).

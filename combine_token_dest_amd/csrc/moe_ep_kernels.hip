@@ -631,6 +631,30 @@ struct CombineHead {
   int32_t chunks;
 };
 
+// The argument set of the compact combine launch (combine_kernel_compact):
+// outputs at a constant stride instead of a per-rank table.
+struct CompactCombine {
+  int32_t tpr;
+  uint8_t* out_base;
+  int64_t out_stride;
+};
+
+// Output row base of source rank s.
+template <class A>
+__device__ __forceinline__ uint8_t* output_of(const A& a, const int s) {
+  return a.output[s];
+}
+__device__ __forceinline__ uint8_t* output_of(const CompactCombine& a, const int s) {
+  return a.out_base + (int64_t)s * a.out_stride;
+}
+
+// Expert-output base of rank d: from the base and stride, or the per-rank table.
+template <bool STRIDED, class A>
+__device__ __forceinline__ const uint8_t* expert_output_of(const A& a, const CombineHead& h, const int d) {
+  if constexpr (STRIDED) return h.eo_base + (int64_t)d * h.eo_stride;
+  else return a.expert_output[d];
+}
+
 template <int DT, int VE, int U, int DB, int LP, int SP, bool ONEPASS, bool STRIDED, bool DEVN, bool GL, class A>
 __device__ __forceinline__ void combine_token(const A& a, const CombineHead& h, const int b,
                                               const int chunk, const bool store) {
@@ -638,7 +662,7 @@ __device__ __forceinline__ void combine_token(const A& a, const CombineHead& h, 
   int s;
   int t;
   uint64_t m;
-  if (DEVN) {
+  if constexpr (DEVN) {
     // Slots of every possible token (b = s*tpr + t); those past the count
     // dispatch used hold none.
     s = (int)(((uint64_t)b * a.tpr_div.magic) >> a.tpr_div.shift);
@@ -659,7 +683,7 @@ __device__ __forceinline__ void combine_token(const A& a, const CombineHead& h, 
   const int64_t row_bytes = h.hidden * esz;
   const int64_t per_block = (int64_t)h.block * U;
   constexpr int VB = VE * esz;
-  const __amdgpu_buffer_rsrc_t out = row_rsrc(a.output[s] + (int64_t)t * row_bytes, row_bytes);
+  const __amdgpu_buffer_rsrc_t out = row_rsrc(output_of(a, s) + (int64_t)t * row_bytes, row_bytes);
 
   auto pass = [&](const int64_t c0) {
     // Lanes past the end of the row read column 0 (in bounds) and store
@@ -692,10 +716,7 @@ __device__ __forceinline__ void combine_token(const A& a, const CombineHead& h, 
         // (the call sites never make one), so slot 0 is always a routed row
         // and every other slot is a routed row or a copy of the one before.
         if (mm == 0) return;
-        auto row_of = [&](const int d) {
-          const uint8_t* eo = STRIDED ? h.eo_base + (int64_t)d * h.eo_stride : a.expert_output[d];
-          return eo + r * row_bytes;
-        };
+        auto row_of = [&](const int d) { return expert_output_of<STRIDED>(a, h, d) + r * row_bytes; };
         const uint8_t* rows[DBX];
         rows[0] = row_of(__builtin_ctzll(mm));
         mm &= mm - 1;
@@ -725,8 +746,7 @@ __device__ __forceinline__ void combine_token(const A& a, const CombineHead& h, 
           if (mm) {
             const int d = __builtin_ctzll(mm);
             mm &= mm - 1;
-            const uint8_t* eo = STRIDED ? h.eo_base + (int64_t)d * h.eo_stride : a.expert_output[d];
-            rows[k] = row_rsrc(eo + r * row_bytes, row_bytes);
+            rows[k] = row_rsrc(expert_output_of<STRIDED>(a, h, d) + r * row_bytes, row_bytes);
             cnt = k + 1;
           } else if (k > 0) {
             rows[k] = rows[k - 1];
@@ -777,34 +797,65 @@ __device__ __forceinline__ void combine_token(const A& a, const CombineHead& h, 
 // token on one XCD made these small workgroups 5% faster on the
 // DeepSeek-V3-shaped round than one 896-thread workgroup per token; placed
 // round-robin they were no faster.
+// One workgroup per item, no grid-stride loop: with stores ahead of it in
+// the same workgroup the token-record load could not be a scalar load.
+// Every test or argument load between the start and the first row load
+// costs the workgroup another dependent round trip, hence: the leading
+// arguments arrive preloaded, i / 8 / chunks is a multiply and a shift,
+// DEVN (device-resident counts) and STRIDED are instantiations, and a slot
+// past the last token (the grid holds whole groups of 8) repeats the last
+// token's loads and stores nothing instead of returning.
+// Row loads (GL): through plain global addresses for groups of up to
+// kSmallGroup ranks, through one buffer resource per row above that.  In
+// interleaved runs the global loads made the DeepSeek-V3 round's combine
+// 1.1% faster (16.54 against 16.71-16.76 us, two boxes) and a ragged 8-rank
+// one 0.6%, but a 32-rank round's 3% slower (95.1-95.4 against 92.4-93.0
+// us); a 16-rank fp8 one was even.
+template <int DT, int VE, int U, int DB, int LP, int SP, bool ONEPASS, bool STRIDED, bool DEVN, bool GL, class A>
+__device__ __forceinline__ void combine_item(const A& a, const uint64_t chunk_magic, const uint32_t chunk_shift,
+                                             const int32_t ntok, const CombineHead& h) {
+  const int i = blockIdx.x;
+  const int rest = i >> 3;
+  const int q = (int)(((uint64_t)rest * chunk_magic) >> chunk_shift);
+  const int chunk = rest - q * h.chunks;
+  const int b = q * 8 + (i & 7);
+  const bool real = b < ntok;
+  combine_token<DT, VE, U, DB, LP, SP, ONEPASS, STRIDED, DEVN, GL>(a, h, real ? b : ntok - 1, chunk, real);
+}
+
 template <int DT, int VE, int U, int DB, int LP, int SP, bool ONEPASS, bool STRIDED, bool DEVN, int MR>
 __global__ void __launch_bounds__(kMaxCombineBlock)
 combine_kernel(const uint64_t chunk_magic, const uint32_t chunk_shift, const int32_t ntok, const int32_t chunks,
                const int32_t block, const TokenRec* tokens, const uint8_t* eo_base, const int64_t eo_stride,
                const int64_t hidden, const CombineArgs<MR> a) {
-  // One workgroup per item, no grid-stride loop: with stores ahead of it in
-  // the same workgroup the token-record load could not be a scalar load.
-  // Every test or argument load between the start and the first row load
-  // costs the workgroup another dependent round trip, hence: the leading
-  // arguments arrive preloaded, i / 8 / chunks is a multiply and a shift,
-  // DEVN (device-resident counts) and STRIDED are instantiations, and a
-  // slot past the last token (the grid holds whole groups of 8) repeats the
-  // last token's loads and stores nothing instead of returning.
-  const int i = blockIdx.x;
-  const int rest = i >> 3;
-  const int q = (int)(((uint64_t)rest * chunk_magic) >> chunk_shift);
-  const int chunk = rest - q * chunks;
-  const int b = q * 8 + (i & 7);
-  const bool real = b < ntok;
   const CombineHead h{tokens, eo_base, eo_stride, hidden, block, chunks};
-  // Row loads: through plain global addresses for groups of up to
-  // kSmallGroup ranks, through one buffer resource per row above that.  In
-  // interleaved runs the global loads made the DeepSeek-V3 round's combine
-  // 1.1% faster (16.54 against 16.71-16.76 us, two boxes) and a ragged
-  // 8-rank one 0.6%, but a 32-rank round's 3% slower (95.1-95.4 against
-  // 92.4-93.0 us); a 16-rank fp8 one was even.
-  combine_token<DT, VE, U, DB, LP, SP, ONEPASS, STRIDED, DEVN, (MR <= kSmallGroup)>(a, h, real ? b : ntok - 1, chunk,
-                                                                                   real);
+  combine_item<DT, VE, U, DB, LP, SP, ONEPASS, STRIDED, DEVN, (MR <= kSmallGroup)>(a, chunk_magic, chunk_shift, ntok, h);
+}
+
+// The same combine for host-count steps whose expert outputs and outputs
+// both lie at constant strides: every argument is a scalar (80 bytes in
+// all), and the HIP runtime on this stack enqueues a launch with at most
+// ~96 bytes of arguments ~0.6 us faster than one with 128 or more (host
+// time per call 2.6-2.7 against 3.2-3.4 us), which is most of a
+// decode-size round's cost.
+template <int DT, int VE, int U, int DB, int LP, int SP, bool ONEPASS, bool GL>
+__global__ void __launch_bounds__(kMaxCombineBlock)
+combine_kernel_compact(const uint64_t chunk_magic, const uint32_t chunk_shift, const int32_t ntok,
+                       const int32_t chunks, const int32_t block, const TokenRec* tokens, const uint8_t* eo_base,
+                       const int64_t eo_stride, const int64_t hidden, uint8_t* out_base, const int64_t out_stride,
+                       const int32_t tpr) {
+  const CombineHead h{tokens, eo_base, eo_stride, hidden, block, chunks};
+  const CompactCombine a{tpr, out_base, out_stride};
+  combine_item<DT, VE, U, DB, LP, SP, ONEPASS, true, false, GL>(a, chunk_magic, chunk_shift, ntok, h);
+}
+
+template <int DT, int VE>
+const void* pick_combine_compact(bool onepass, bool gl) {
+#define MOE_EP_CC(OP, G) \
+  reinterpret_cast<const void*>(&combine_kernel_compact<DT, VE, kCombineU, kCombineDB, kCombineLP, kCombineSP, OP, G>)
+  if (onepass) return gl ? MOE_EP_CC(true, true) : MOE_EP_CC(true, false);
+  return gl ? MOE_EP_CC(false, true) : MOE_EP_CC(false, false);
+#undef MOE_EP_CC
 }
 
 template <int DT, int VE, int MR>
@@ -939,13 +990,20 @@ hipError_t launch_combine(const CombineKArgs& args, int dtype, int vec_elems, hi
   const bool strided = common_stride(a.expert_output, a.ep, &a.eo_base, &a.eo_stride);
   const bool devn = a.dev_counts != nullptr;
   const bool small = a.ep <= kSmallGroup;
+  // Host-count steps with expert outputs and outputs at constant strides
+  // take the compact launch (all-scalar arguments).
+  const uint8_t* out_base = nullptr;
+  int64_t out_stride = 0;
+  const bool compact =
+      !devn && strided && common_stride(const_cast<const uint8_t* const*>(a.output), a.ep, &out_base, &out_stride);
   a.block = sh.block;
   a.chunk_div = make_owner_div((uint32_t)a.chunks);
   if (devn) a.tpr_div = make_owner_div((uint32_t)a.tpr);
 #define MOE_EP_C(DT, VE) \
     case VE: \
-      fn = small ? pick_combine<DT, VE, kSmallGroup>(onepass, strided, devn) \
-                 : pick_combine<DT, VE, kMaxRanks>(onepass, strided, devn); \
+      fn = compact ? pick_combine_compact<DT, VE>(onepass, small) \
+           : small ? pick_combine<DT, VE, kSmallGroup>(onepass, strided, devn) \
+                   : pick_combine<DT, VE, kMaxRanks>(onepass, strided, devn); \
       break;
   if (dtype == MOE_EP_F32) {
     switch (vec_elems) {
@@ -973,6 +1031,12 @@ hipError_t launch_combine(const CombineKArgs& args, int dtype, int vec_elems, hi
   const uint8_t* eo_base = a.eo_base;
   int64_t eo_stride = a.eo_stride;
   int64_t hidden = a.hidden;
+  if (compact) {
+    uint8_t* obase = const_cast<uint8_t*>(out_base);
+    void* cargs[] = {&magic, &shift, &a.ntok, &a.chunks, &a.block, &tokens, &eo_base, &eo_stride, &hidden,
+                     &obase, &out_stride, &a.tpr};
+    return hipLaunchKernel(fn, dim3(sh.grid_x), dim3(sh.block), cargs, (size_t)sh.lds, stream);
+  }
   CombineArgs<kSmallGroup> sa;
   if (small) sa = small_args(a);
   void* kargs[] = {&magic, &shift, &a.ntok, &a.chunks, &a.block, &tokens, &eo_base, &eo_stride, &hidden,

@@ -281,7 +281,9 @@ class MoEEp:
         ``[ep*tpr, hidden]`` or ``[ep, tpr, hidden]``; None means rank d's
         combine input buffer.  When every entry is None the element type is
         the output's, else the one last requested from
-        get_combine_input_buffer() this round, else bfloat16."""
+        get_combine_input_buffer() this round, else bfloat16.  Outputs not
+        passed are returned as slices [s, :n_s] of one new
+        [ep, max n_s, hidden] tensor."""
         if self._handle is None:
             raise RuntimeError("MoEEp has been destroyed")
         p = self.params
@@ -310,11 +312,17 @@ class MoEEp:
                 raise ValueError(f"rank {d}: expert_output must be {dtype} [{rows}, {p.hidden_size}]")
             a_eo[d] = _dev_ptr(t, self.device, f"expert_output[{d}]")
         outs = []
+        # Outputs the caller leaves to us are slices [s, :n_s] of one
+        # allocation: at a constant stride, so the library can take its
+        # compact launch (all-scalar kernel arguments, cheaper to enqueue).
+        fresh = None
+        if output is None or any(o is None for o in output):
+            fresh = torch.empty((ep, max(self._n), p.hidden_size), dtype=dtype, device=self.device)
         for s in range(ep):
             ns = self._n[s]
             o = output[s] if output is not None else None
             if o is None:
-                o = torch.empty((ns, p.hidden_size), dtype=dtype, device=self.device)
+                o = fresh[s, :ns]
             elif o.dtype != dtype or tuple(o.shape) != (ns, p.hidden_size):
                 raise ValueError(f"rank {s}: output must be {dtype} [{ns}, {p.hidden_size}]")
             a_out[s] = _dev_ptr(o, self.device, f"output[{s}]") if ns else None

@@ -226,7 +226,11 @@ MOE_EP_API int moe_ep_get_combine_input_buffer(moe_ep_handle handle, int32_t ran
  * rank gets zeros.  Rows of tokens not dispatched to d are never read, nor is
  * any row of a masked-off rank (MoEEpCommunication, combine();
  * NVLinkOneSidedAlltoAll, combine() mask rule).  Needs the DISPATCHED state;
- * leaves the handle IDLE.  One kernel launch. */
+ * leaves the handle IDLE.  One kernel launch.  After a host-count dispatch,
+ * when the read ranks' expert_output rows and the non-empty outputs each lie
+ * at one constant stride (the combine input buffers do; so do outputs sliced
+ * from one [ep_size, n, hidden_size] allocation), the launch carries only
+ * scalar arguments, which the HIP runtime enqueues ~0.6 us faster. */
 MOE_EP_API int moe_ep_combine(moe_ep_handle handle, const moe_ep_combine_args* args, void* stream);
 
 /* Releases the handle's host state; a workspace passed to moe_ep_create

@@ -565,6 +565,52 @@ def test_combine_input_layouts(layout):
     moe.destroy()
 
 
+@pytest.mark.parametrize("layout", ["forward", "reverse", "uneven", "misaligned", "empty_ranks", "one_rank"])
+def test_combine_output_layouts(layout):
+    """Outputs placed in one buffer in different layouts, the inputs in the
+    combine input buffers.  Outputs at a constant stride (forward, reverse,
+    misaligned; with empty ranks, whose outputs are NULL and do not count;
+    a single rank with tokens) take the compact launch, the uneven layout
+    the per-rank output table.  Every output row matches the oracle and no
+    byte between the outputs is written."""
+    log(f"[parity] combine output layout {layout}")
+    w = dataclasses.replace(wl.BY_NAME["dsv3"], max_tokens_per_rank=16)
+    nt = {"empty_ranks": [16, 0, 3, 16, 0, 0, 9, 1], "one_rank": [0, 0, 0, 0, 0, 11, 0, 0]}.get(layout)
+    c = parity.case_from_workload(w, local_num_tokens=nt, seed=7300)
+    p = parity.oracle_params(c)
+    om = oracle.OracleMoEEp(p)
+    ores = om.dispatch(c.hidden, c.ids, c.weights)
+    eo_host = parity.combine_inputs_host(c, ores)
+    oout = om.combine(eo_host, c.combine_dtype)
+    moe = parity.make_gpu(c)
+    hid, ids, wt, _ = parity.upload(c)
+    moe.dispatch(hid, ids, wt)
+    for d in range(c.ep):
+        buf = moe.get_combine_input_buffer(d, torch.bfloat16)
+        buf.copy_(parity.host_to_torch(eo_host[d], c.combine_dtype).view(buf.shape))
+    hs, ep, n = c.hidden_size, c.ep, c.n
+    stride = c.cap * hs + 512                  # elements between consecutive outputs
+    if layout == "reverse":
+        offs = [(ep - 1 - s) * stride for s in range(ep)]
+    elif layout == "uneven":
+        offs = [s * stride + 64 * s * s for s in range(ep)]
+    elif layout == "misaligned":
+        offs = [s * stride + 1 for s in range(ep)]
+    else:
+        offs = [s * stride for s in range(ep)]
+    canary = -1024.0
+    big = torch.full((max(offs) + stride + 8,), canary, dtype=torch.bfloat16, device="cuda")
+    outs = [big[offs[s]:offs[s] + n[s] * hs].view(n[s], hs) for s in range(ep)]
+    gout = moe.combine([None] * ep, output=outs)
+    torch.cuda.synchronize()
+    parity.compare_combine(c, gout, oout, f"output layout {layout}")
+    written = torch.zeros(big.numel(), dtype=torch.bool, device="cuda")
+    for s in range(ep):
+        written[offs[s]:offs[s] + n[s] * hs] = True
+    assert bool((big[~written] == canary).all()), "combine wrote outside its output rows"
+    moe.destroy()
+
+
 @pytest.mark.parametrize("ep,cap,nt", [(3, 5, [5, 0, 3]), (5, 7, [7, 1, 0, 6, 2])])
 @pytest.mark.parametrize("order", ORDERS)
 def test_device_counts_with_a_partial_slot_group(ep, cap, nt, order):

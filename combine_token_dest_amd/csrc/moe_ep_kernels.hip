@@ -631,7 +631,7 @@ struct CombineHead {
   int32_t chunks;
 };
 
-// The argument set of the compact combine launch (combine_kernel_compact):
+// The argument set of the compact combine launch (the all-scalar combine_kernel):
 // outputs at a constant stride instead of a per-rank table.
 struct CompactCombine {
   int32_t tpr;
@@ -833,14 +833,14 @@ combine_kernel(const uint64_t chunk_magic, const uint32_t chunk_shift, const int
 }
 
 // The same combine for host-count steps whose expert outputs and outputs
-// both lie at constant strides: every argument is a scalar (80 bytes in
-// all), and the HIP runtime on this stack enqueues a launch with at most
-// ~96 bytes of arguments ~0.6 us faster than one with 128 or more (host
-// time per call 2.6-2.7 against 3.2-3.4 us), which is most of a
-// decode-size round's cost.
+// both lie at constant strides (an overload of the kernel template above):
+// every argument is a scalar (80 bytes in all), and the HIP runtime on this
+// stack enqueues a launch with at most ~96 bytes of arguments ~0.6 us
+// faster than one with 128 or more (host time per call 2.6-2.7 against
+// 3.2-3.4 us).
 template <int DT, int VE, int U, int DB, int LP, int SP, bool ONEPASS, bool GL>
 __global__ void __launch_bounds__(kMaxCombineBlock)
-combine_kernel_compact(const uint64_t chunk_magic, const uint32_t chunk_shift, const int32_t ntok,
+combine_kernel(const uint64_t chunk_magic, const uint32_t chunk_shift, const int32_t ntok,
                        const int32_t chunks, const int32_t block, const TokenRec* tokens, const uint8_t* eo_base,
                        const int64_t eo_stride, const int64_t hidden, uint8_t* out_base, const int64_t out_stride,
                        const int32_t tpr) {
@@ -852,7 +852,7 @@ combine_kernel_compact(const uint64_t chunk_magic, const uint32_t chunk_shift, c
 template <int DT, int VE>
 const void* pick_combine_compact(bool onepass, bool gl) {
 #define MOE_EP_CC(OP, G) \
-  reinterpret_cast<const void*>(&combine_kernel_compact<DT, VE, kCombineU, kCombineDB, kCombineLP, kCombineSP, OP, G>)
+  reinterpret_cast<const void*>(&combine_kernel<DT, VE, kCombineU, kCombineDB, kCombineLP, kCombineSP, OP, G>)
   if (onepass) return gl ? MOE_EP_CC(true, true) : MOE_EP_CC(true, false);
   return gl ? MOE_EP_CC(false, true) : MOE_EP_CC(false, false);
 #undef MOE_EP_CC

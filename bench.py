@@ -347,7 +347,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--workload", default="dsv3", choices=["tiny", "dsv3", "fp8", "ragged", "large"])
     ap.add_argument("--tokens-per-rank", type=int, default=None,
                     help="the workload at another capacity (tokens per rank), e.g. decode batch sizes")
     ap.add_argument("--instances", type=int, default=8)
@@ -369,6 +369,8 @@ def main():
                     help="skip the HIP graph replays after the timed passes (profiled runs: the kernel "
                          "trace then holds only the set-up, warm-up and timed launches)")
     args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0 or args.instances < 1 or args.kernel_steps < 1:
+        ap.error("--steps, --instances and --kernel-steps must be at least 1, --warmup at least 0")
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -14,6 +14,7 @@ mask notes of dispatch() and combine()).
 from __future__ import annotations
 
 from dataclasses import dataclass
+from types import SimpleNamespace
 from typing import List, Optional, Sequence
 
 import torch
@@ -56,12 +57,16 @@ class _DeviceBytes:
                                          "strides": None, "version": 3}
 
 
-def _dev_ptr(t: torch.Tensor, device: torch.device, what: str) -> int:
-    # get_device() is the cheap form of the device check (-1 for CPU tensors)
-    if t.get_device() != device.index or not t.is_cuda:
-        raise ValueError(f"{what} is on {t.device}, expected {device}")
+def _dev_ptr(t: torch.Tensor, dev_index: int, what: str, rank: Optional[int] = None) -> int:
+    """Address of a contiguous tensor on GPU ``dev_index``; the argument's
+    name (``what``, with ``[rank]``) is only formatted for an error."""
+    # get_device() is -1 for CPU tensors, so it is the whole device check
+    if t.get_device() != dev_index:
+        name = what if rank is None else f"{what}[{rank}]"
+        raise ValueError(f"{name} is on {t.device}, expected cuda:{dev_index}")
     if not t.is_contiguous():
-        raise ValueError(f"{what} must be contiguous")
+        name = what if rank is None else f"{what}[{rank}]"
+        raise ValueError(f"{name} must be contiguous")
     return t.data_ptr()
 
 
@@ -94,6 +99,9 @@ class MoEEp:
             scale_row_bytes=scale_row_bytes, invalid_expert_id=invalid_expert_id,
             enable_rank_mask=1 if enable_rank_mask else 0, eplb_stats_bytes=eplb_stats_bytes,
             dispatch_order=_ORDERS[dispatch_order] if isinstance(dispatch_order, str) else int(dispatch_order))
+        # the sizes as plain ints (a ctypes field read costs more than an attribute)
+        self._p = SimpleNamespace(**{f: getattr(self.params, f) for f, _ in _lib.moe_ep_params._fields_})
+        self._dev_index = self.device.index
         self.checkpointable = checkpointable
         if checkpointable:
             # The library maps the workspace itself (HIP virtual memory), so
@@ -166,7 +174,8 @@ class MoEEp:
         array (steps of at most MOE_EP_NOALLOC_MAX_ROWS receive rows)."""
         if self._handle is None:
             raise RuntimeError("MoEEp has been destroyed")
-        p = self.params
+        p = self._p
+        di = self._dev_index
         ep = p.ep_size
         if len(hidden_states) != ep or len(topk_ids) != ep:
             raise ValueError(f"expected {ep} per-rank hidden_states and topk_ids")
@@ -192,21 +201,21 @@ class MoEEp:
                 raise ValueError(f"rank {s}: hidden_states must be {ns} rows of {p.hidden_row_bytes} bytes")
             n.append(ns)
             a_n[s] = ns
-            a_hidden[s] = _dev_ptr(h, self.device, f"hidden_states[{s}]") if ns else None
-            a_ids[s] = _dev_ptr(ids, self.device, f"topk_ids[{s}]") if ns else None
+            a_hidden[s] = _dev_ptr(h, di, "hidden_states", s) if ns else None
+            a_ids[s] = _dev_ptr(ids, di, "topk_ids", s) if ns else None
             if topk_weights is not None and topk_weights[s] is not None:
                 w = topk_weights[s]
                 if w.dtype != torch.float32 or tuple(w.shape) != (ns, p.top_k):
                     raise ValueError(f"rank {s}: topk_weights must be float32 [{ns}, {p.top_k}]")
                 wp |= 1 << s
-                a_w[s] = _dev_ptr(w, self.device, f"topk_weights[{s}]") if ns else None
+                a_w[s] = _dev_ptr(w, di, "topk_weights", s) if ns else None
             if hidden_states_scale is not None and hidden_states_scale[s] is not None:
                 sc = hidden_states_scale[s]
                 if sc.shape[0] != ns or sc.numel() * sc.element_size() != ns * p.scale_row_bytes:
                     raise ValueError(f"rank {s}: hidden_states_scale must be {ns} rows of "
                                      f"{p.scale_row_bytes} bytes")
                 sp |= 1 << s
-                a_scale[s] = _dev_ptr(sc, self.device, f"hidden_states_scale[{s}]") if ns else None
+                a_scale[s] = _dev_ptr(sc, di, "hidden_states_scale", s) if ns else None
         ep_present = 0
         if eplb_local_stats is not None:
             if len(eplb_local_stats) != ep:
@@ -218,7 +227,7 @@ class MoEEp:
                 if st.numel() * st.element_size() != p.eplb_stats_bytes:
                     raise ValueError(f"rank {s}: eplb_local_stats must hold {p.eplb_stats_bytes} bytes")
                 ep_present |= 1 << s
-                a.eplb_local_stats[s] = _dev_ptr(st, self.device, f"eplb_local_stats[{s}]")
+                a.eplb_local_stats[s] = _dev_ptr(st, di, "eplb_local_stats", s)
         a.eplb_present = ep_present
         a.weights_present = wp
         a.scales_present = sp
@@ -229,7 +238,7 @@ class MoEEp:
             bound = p.max_tokens_per_rank if runtime_max_tokens_per_rank is None else int(runtime_max_tokens_per_rank)
             if min(n) < bound:
                 raise ValueError(f"with device token counts every rank's buffers must hold {bound} rows")
-            a.local_num_tokens_device = _dev_ptr(t, self.device, "local_num_tokens_device")
+            a.local_num_tokens_device = _dev_ptr(t, di, "local_num_tokens_device")
             n = [bound] * ep
         a.runtime_max_tokens_per_rank = -1 if runtime_max_tokens_per_rank is None \
             else int(runtime_max_tokens_per_rank)
@@ -271,7 +280,7 @@ class MoEEp:
             raise TypeError(f"combine dtype must be float32, bfloat16 or float16, got {dtype}")
         ptr = _lib.moe_ep_get_combine_input_buffer(self._handle, rank, _COMBINE_DTYPES[dtype])
         self._buffer_dtype = dtype
-        return self._view(ptr, self.params.ep_size * self._tpr, self.params.hidden_size * dtype.itemsize, dtype)
+        return self._view(ptr, self._p.ep_size * self._tpr, self._p.hidden_size * dtype.itemsize, dtype)
 
     def combine(self, expert_output: Sequence[Optional[torch.Tensor]], *,
                 output: Optional[Sequence[Optional[torch.Tensor]]] = None,
@@ -286,7 +295,8 @@ class MoEEp:
         [ep, max n_s, hidden] tensor."""
         if self._handle is None:
             raise RuntimeError("MoEEp has been destroyed")
-        p = self.params
+        p = self._p
+        di = self._dev_index
         ep = p.ep_size
         if len(expert_output) != ep:
             raise ValueError(f"expected {ep} per-rank expert_output tensors")
@@ -310,7 +320,7 @@ class MoEEp:
                 continue
             if t.dtype != dtype or t.numel() != rows * p.hidden_size:
                 raise ValueError(f"rank {d}: expert_output must be {dtype} [{rows}, {p.hidden_size}]")
-            a_eo[d] = _dev_ptr(t, self.device, f"expert_output[{d}]")
+            a_eo[d] = _dev_ptr(t, di, "expert_output", d)
         outs = []
         # Outputs the caller leaves to us are slices [s, :n_s] of one
         # allocation: at a constant stride, so the library can take its
@@ -325,7 +335,7 @@ class MoEEp:
                 o = fresh[s, :ns]
             elif o.dtype != dtype or tuple(o.shape) != (ns, p.hidden_size):
                 raise ValueError(f"rank {s}: output must be {dtype} [{ns}, {p.hidden_size}]")
-            a_out[s] = _dev_ptr(o, self.device, f"output[{s}]") if ns else None
+            a_out[s] = _dev_ptr(o, di, "output", s) if ns else None
             outs.append(o)
         a.dtype = _COMBINE_DTYPES[dtype]
         a.active_rank_mask = _mask_value(active_rank_mask)

@@ -694,6 +694,28 @@ def test_call_protocol_errors_leave_state_unchanged():
     moe.destroy()
 
 
+def test_wrapper_rejects_host_and_strided_tensors():
+    """MoEEp refuses a CPU tensor or a non-contiguous one, naming the
+    argument and rank, before anything reaches the library."""
+    log("[parity] wrapper argument checks")
+    c = random_case(5, ep=4, E=8, K=2, cap=8, n=[8, 2, 0, 5], hidden_size=32, H=64)
+    moe = parity.make_gpu(c)
+    hid, ids, w, _ = parity.upload(c)
+    bad = list(hid)
+    bad[1] = hid[1].cpu()
+    with pytest.raises(ValueError, match=r"hidden_states\[1\] is on cpu"):
+        moe.dispatch(bad, ids, w)
+    strided = list(w)
+    strided[3] = torch.empty((c.n[3], 2 * c.K), dtype=torch.float32, device="cuda")[:, ::2]
+    with pytest.raises(ValueError, match=r"topk_weights\[3\] must be contiguous"):
+        moe.dispatch(hid, ids, strided)
+    moe.dispatch(hid, ids, w)                  # nothing was enqueued: the handle is still idle
+    outs = moe.combine([moe.get_combine_input_buffer(d, torch.bfloat16) for d in range(c.ep)])
+    torch.cuda.synchronize()
+    assert [tuple(o.shape) for o in outs] == [(8, 32), (2, 32), (0, 32), (5, 32)]
+    moe.destroy()
+
+
 def test_two_instances_interleaved():
     log("[parity] two instances")
     c1 = parity.case_from_workload(wl.BY_NAME["tiny"])
